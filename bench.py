@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the streaming-video-DiT attention core on one MI355X.
+
+One step = one layer-chunk of the hot path on seeded synthetic inputs already
+resident in HBM:
+    qknorm_rope3d(chunk q, k)            (skipped by the self-attention SR workload)
+    kv_quant_int8(chunk K), (chunk V)    (int8-cache workload: the steady-state cache write)
+    attn_fwd(q, [cache segments..., current chunk])
+
+Prints ONE JSON line. ``value`` is effective attention TFLOP/s of the whole
+step (kept-tile FLOPs 4*d*H*sum rows*cols / step time); ``ms_per_step`` is
+the ms/layer/chunk. ``roofline`` reports the attention kernel alone, timed
+with HIP events around each launch on the stream it runs on.
+``cpu_baseline`` times the fp64 oracle on the host (heads processed one by
+one until about 10 s have elapsed, scaled to TFLOP/s).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "attention ms/layer/chunk + effective TFLOP/s (% bf16 MFMA peak), 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def _dev(a, torch):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+class Step:
+    """Device buffers and the launch sequence of one layer-chunk."""
+
+    def __init__(self, cfg: W.Config, torch, sdit):
+        self.cfg, self.torch, self.sdit = cfg, torch, sdit
+        inp = W.make_inputs(cfg)
+        self.inp = inp
+        H, d, n = cfg.n_heads, cfg.head_dim, cfg.n_q
+        self.q_in, self.k_in, self.v = _dev(inp.q, torch), _dev(inp.k, torch), _dev(inp.v, torch)
+        self.gq, self.gk = _dev(inp.gamma_q, torch), _dev(inp.gamma_k, torch)
+        self.q = torch.empty_like(self.q_in)
+        self.k = torch.empty_like(self.k_in)
+        self.out = torch.empty((n, H, d), dtype=torch.int16, device="cuda")
+        self.lse = torch.empty((H, n), dtype=torch.float32, device="cuda")
+        self.mask = _dev(inp.mask, torch)
+        self.keep = []
+        segs = []
+        for i, (kc, vc) in enumerate(zip(inp.cache_k, inp.cache_v)):
+            kd, vd = _dev(kc, torch), _dev(vc, torch)
+            L = kc.shape[0]
+            if cfg.seg_int8[i]:
+                ck = torch.empty((L, H, d), dtype=torch.int8, device="cuda")
+                cv = torch.empty((L, H, d), dtype=torch.int8, device="cuda")
+                sk = torch.empty((L, H), dtype=torch.float32, device="cuda")
+                sv = torch.empty((L, H), dtype=torch.float32, device="cuda")
+                sdit.kv_quant_int8(kd, ck, sk, L, H, d)
+                sdit.kv_quant_int8(vd, cv, sv, L, H, d)
+                self.keep += [ck, cv, sk, sv]
+                segs.append(dict(k=ck, v=cv, k_scale=sk, v_scale=sv, len=L, dtype=sdit.SDIT_INT8))
+            else:
+                self.keep += [kd, vd]
+                segs.append(dict(k=kd, v=vd, len=L, dtype=sdit.SDIT_BF16))
+        cur_k = self.k if cfg.rope else self.k_in
+        segs.append(dict(k=cur_k, v=self.v, len=n, dtype=sdit.SDIT_BF16))
+        self.segs = sdit.make_segments(segs)
+        self.n_segs = len(segs)
+        self.q_attn = self.q if cfg.rope else self.q_in
+        self.quant_chunk = any(cfg.seg_int8)
+        if self.quant_chunk:
+            self.ck = torch.empty((n, H, d), dtype=torch.int8, device="cuda")
+            self.cv = torch.empty((n, H, d), dtype=torch.int8, device="cuda")
+            self.sk = torch.empty((n, H), dtype=torch.float32, device="cuda")
+            self.sv = torch.empty((n, H), dtype=torch.float32, device="cuda")
+        self.flops = W.attn_flops(cfg, inp.mask)
+        torch.cuda.synchronize()
+
+    def run(self, ev_before=None, ev_after=None):
+        cfg, sdit = self.cfg, self.sdit
+        H, d, n = cfg.n_heads, cfg.head_dim, cfg.n_q
+        if cfg.rope:
+            dt, dh, dw = cfg.split
+            sdit.qknorm_rope3d(self.q_in, self.k_in, self.q, self.k, self.gq, self.gk, cfg.T, cfg.Hl, cfg.Wl,
+                               cfg.t0, H, d, dt, dh, dw, cfg.theta, cfg.eps)
+        if self.quant_chunk:
+            sdit.kv_quant_int8(self.k, self.ck, self.sk, n, H, d)
+            sdit.kv_quant_int8(self.v, self.cv, self.sv, n, H, d)
+        if ev_before is not None:
+            ev_before.record()
+        sdit.attn_fwd(self.q_attn, n, self.segs, self.mask, cfg.block, cfg.block, H, d, self.out, self.lse)
+        if ev_after is not None:
+            ev_after.record()
+
+
+def cpu_baseline(cfg: W.Config, budget_s: float = 10.0):
+    """The oracle as it stands, on the host: qknorm_rope3d of the chunk (and
+    the int8 quantisation of the cache for the int8 workload) once, then
+    attention head by head until ``budget_s`` has elapsed. Scaled to TFLOP/s
+    over the heads done, with the one-off work charged in full."""
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    inp = W.make_inputs(cfg)
+    t0 = time.perf_counter()
+    if cfg.rope:
+        dt, dh, dw = cfg.split
+        rq = oracle.qknorm_rope3d(inp.q, inp.gamma_q, cfg.T, cfg.Hl, cfg.Wl, cfg.t0, dt, dh, dw)
+        rk = oracle.qknorm_rope3d(inp.k, inp.gamma_k, cfg.T, cfg.Hl, cfg.Wl, cfg.t0, dt, dh, dw)
+    else:
+        rq, rk = inp.q, inp.k
+    segs = []
+    for i, (k, v) in enumerate(zip(inp.cache_k, inp.cache_v)):
+        if cfg.seg_int8[i]:
+            ck, sk = oracle.kv_quant_int8(k)
+            cv, sv = oracle.kv_quant_int8(v)
+            segs.append({"k": ck, "v": cv, "k_scale": sk, "v_scale": sv, "dtype": "int8"})
+        else:
+            segs.append({"k": k, "v": v, "dtype": "bf16"})
+    segs.append({"k": rk, "v": inp.v, "dtype": "bf16"})
+    heads = 0
+    while heads < cfg.n_heads:
+        oracle.attention(rq, segs, inp.mask, cfg.block, cfg.block, heads=[heads])
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    flops = W.attn_flops(cfg, inp.mask) * heads / cfg.n_heads
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{cfg.name}: qknorm_rope3d of the whole chunk"
+                      f"{' + int8 quantisation of the cache' if any(cfg.seg_int8) else ''}"
+                      f" + attention for {heads} of {cfg.n_heads} heads, fp64 numpy, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="wan13b", choices=sorted(W.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the kernel runs on one GPU's share; sharding is described in the design notes).",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import streaming_video_dit_amd as sdit
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    cfg = W.CONFIGS[args.workload]
+    step = Step(cfg, torch, sdit)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    # determinism: the output of two identical steps must be bit-identical
+    h1 = hashlib.md5(step.out.cpu().numpy().tobytes()).hexdigest()
+    step.run()
+    torch.cuda.synchronize()
+    h2 = hashlib.md5(step.out.cpu().numpy().tobytes()).hexdigest()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step.run(*evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg = float(np.mean(attn_ms))
+    value = step.flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = step.flops / (attn_avg * 1e-3) / 1e12
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "description": cfg.description, "n_heads": cfg.n_heads,
+                   "head_dim": cfg.head_dim, "n_q": cfg.n_q, "segments": cfg.seg_lens,
+                   "int8_segments": cfg.seg_int8, "block": cfg.block,
+                   "kept_tiles": int(step.inp.mask.sum()), "mask_tiles": int(step.inp.mask.size),
+                   "effective_gflop": round(step.flops / 1e9, 3), "parallelism": "none (1 GPU)"},
+        "attn_ms": round(attn_avg, 5),
+        "attn_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5), round(float(np.percentile(attn_ms, 90)), 5)],
+        "pct_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "pct_bf16_peak_attn": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "deterministic": h1 == h2,
+        "wall_s_timed": round(t_wall, 3),
+        "roofline": {"kernel": "attn_fwd_kernel<128>" if cfg.head_dim == 128 else "attn_fwd_kernel<64>",
+                     "bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * sdit: attention core of a streaming video diffusion transformer, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * For one chunk of latent-frame query tokens the library
+ *   1. applies QK-RMSNorm and the 3D (t, h, w) rotary embedding to the
+ *      chunk's q and k                       -> sdit_qknorm_rope3d
+ *   2. optionally stores K/V as int8 with one fp32 scale per (token, head)
+ *                                            -> sdit_kv_quant_int8
+ *   3. runs block-masked softmax attention of the queries against a K/V
+ *      cache made of ordered segments, e.g.
+ *      [cached text | history chunks or reference image | current chunk]
+ *                                            -> sdit_attn_fwd
+ *
+ * Conventions shared by every entry point
+ *   - bf16 tensors are passed as raw 16-bit words (upper half of binary32).
+ *   - Token-major layout [tokens][heads][head_dim], head_dim contiguous.
+ *   - Every tensor pointer is DEVICE memory, except `segs` of sdit_attn_fwd,
+ *     which is a HOST array. The caller allocates and frees everything; the
+ *     library allocates nothing and keeps no per-call state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work; nothing synchronises. A fault inside a kernel
+ *     surfaces at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is launched. On
+ *     a validation failure nothing is launched, the call returns a nonzero
+ *     sdit_status and sdit_last_error() describes the problem (the message
+ *     is per thread). Launch failures return SDIT_ERR_DEVICE; a device
+ *     without a gfx950 code object returns SDIT_ERR_UNSUPPORTED.
+ *   - Pointers to bf16/int8 tensors must be 16-byte aligned, fp32 arrays
+ *     4-byte aligned.
+ *   - Inputs must be finite. Only tiles that the block mask skips may hold
+ *     non-finite values (they are never read).
+ */
+#ifndef SDIT_H
+#define SDIT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDIT_ABI_VERSION 1
+#define SDIT_MAX_SEGMENTS 8
+
+typedef enum sdit_status {
+  SDIT_OK = 0,
+  SDIT_ERR_INVALID = 1,     /* bad argument; nothing was launched            */
+  SDIT_ERR_UNSUPPORTED = 2, /* valid request this build/device cannot run    */
+  SDIT_ERR_DEVICE = 3       /* the HIP runtime reported an error at launch   */
+} sdit_status;
+
+typedef enum sdit_dtype {
+  SDIT_BF16 = 0,
+  SDIT_INT8 = 1
+} sdit_dtype;
+
+/* One K/V segment of the attention cache (host struct, device pointers).
+ *   k, v      [len][n_heads][head_dim], bf16 words or int8 codes (dtype)
+ *   k_scale,  [len][n_heads] fp32, int8 segments only (NULL for bf16);
+ *   v_scale   the value of element c is code_c * scale.
+ *   len       number of tokens (0 allowed: the segment is empty)
+ *   dtype     sdit_dtype
+ * Joy-face_change_optimized README, section 1, item 1: attention K/V is the
+ * static text cache + the image cache + the current chunk; the int8 cache
+ * bullet of the same section scales per token and head. */
+typedef struct sdit_kv_segment {
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t len;
+  int32_t dtype;
+} sdit_kv_segment;
+
+int sdit_abi_version(void);
+const char* sdit_status_string(int status);
+const char* sdit_last_error(void);
+
+/* QK-RMSNorm followed by the 3D rotary embedding, for the chunk's q and k.
+ * ("QK-norm+3D RoPE" fused operator: Joy-face_change_optimized README,
+ * table of changed files; cached text keys are stored after the qk-norm,
+ * section 1, item 1.)
+ *
+ * For every token n and head h, over the head dimension d:
+ *   y_c = x_c / sqrt(mean_c(x_c^2) + eps) * gamma_c      (gamma per tensor)
+ * then the head dimension is cut into axis blocks t | h | w of widths
+ * d_t, d_h, d_w (even, summing to head_dim); in an axis block of width d_a,
+ * the interleaved pair (2j, 2j+1) is rotated by the angle
+ *   p_a * theta^(-2j/d_a),
+ * p_a being the token's position on that axis. Tokens are in (t, h, w)
+ * row-major order, w fastest: n -> t = t0 + n/(Hl*Wl), h = (n/Wl) % Hl,
+ * w = n % Wl. Arithmetic is fp32 with one rounding to bf16 at the end.
+ *
+ *   q_in, k_in     bf16 [T*Hl*Wl][n_heads][head_dim]
+ *   q_out, k_out   bf16, same shape; may equal q_in / k_in (in place),
+ *                  must not otherwise overlap any other tensor argument
+ *   gamma_q/_k     fp32 [head_dim]
+ *   head_dim       64 or 128
+ *   theta > 0, eps >= 0, t0 >= 0; T, Hl or Wl == 0 is a no-op. */
+int sdit_qknorm_rope3d(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                       const float* gamma_q, const float* gamma_k,
+                       int32_t T, int32_t Hl, int32_t Wl, int32_t t0,
+                       int32_t n_heads, int32_t head_dim,
+                       int32_t d_t, int32_t d_h, int32_t d_w,
+                       float theta, float eps, void* stream);
+
+/* Symmetric int8 quantisation of a K or V tensor, one fp32 scale per
+ * (token, head) (Joy-face_change_optimized README, section 1, int8 K/V
+ * bullet). Call once for K and once for V.
+ *   amax   = max_c |x_c|
+ *   scale  = amax / 127                      (IEEE binary32 division)
+ *   code_c = clamp(rne(x_c / scale), -127, 127)
+ *            (binary32 quotient, then round half to even)
+ *   amax == 0 -> scale = 0 and all codes 0.
+ *   x       bf16 [n_tok][n_heads][head_dim]
+ *   codes   int8 [n_tok][n_heads][head_dim]
+ *   scales  fp32 [n_tok][n_heads]
+ *   head_dim 64 or 128; n_tok == 0 is a no-op. Outputs must not overlap x. */
+int sdit_kv_quant_int8(const void* x, int8_t* codes, float* scales,
+                       int32_t n_tok, int32_t n_heads, int32_t head_dim, void* stream);
+
+/* Block-masked softmax attention of n_q queries over the concatenation of
+ * the segments (Joy-face_change_optimized README, section 1, item 1;
+ * block-causal chunks: Wave Forcing summary; block-sparse attention with a
+ * (q-block, k-block) mask that, when dense, equals ordinary
+ * scaled-dot-product attention: FlashVSR deployment notes,
+ * Block-Sparse-Attention section).
+ *
+ *   q            bf16 [n_q][n_heads][head_dim] (after sdit_qknorm_rope3d)
+ *   segs         HOST array of n_segs segments, 1 <= n_segs <= 8
+ *   block_mask   uint8 [ceil(n_q/block_q)][sum_s ceil(len_s/block_k)],
+ *                row-major, nonzero = keep. Query i is in row i/block_q.
+ *                k-blocks restart at every segment: key j of segment s is in
+ *                column sum_{s'<s} ceil(len_s'/block_k) + j/block_k, so a
+ *                block never straddles two segments; last blocks may be
+ *                partial.
+ *   block_q, block_k   16, 32, 64 or 128
+ *   head_dim     64 or 128
+ *   softmax_scale  <= 0 selects 1/sqrt(head_dim)
+ *   out          bf16 [n_q][n_heads][head_dim]
+ *   lse          fp32 [n_heads][n_q] natural-log sum of exponentials of the
+ *                scaled scores, or NULL
+ * For query i with visible keys V(i) = {j : mask[qb(i)][kb(j)] != 0}:
+ *   s_j = scale * q_i . k_j,  o_i = sum_j softmax(s)_j v_j,  lse_i = log sum_j e^{s_j};
+ * a query with no visible key gets o_i = 0 and lse_i = -inf.
+ * Output must not overlap any input. */
+int sdit_attn_fwd(const void* q, int32_t n_q,
+                  const sdit_kv_segment* segs, int32_t n_segs,
+                  const uint8_t* block_mask, int32_t block_q, int32_t block_k,
+                  int32_t n_heads, int32_t head_dim, float softmax_scale,
+                  void* out, float* lse, void* stream);
+
+/* Host-only validators: the exact checks the entry points run before a
+ * launch, without touching any device. They return SDIT_OK or the status
+ * the entry point would return, and set sdit_last_error() likewise. */
+int sdit_validate_qknorm_rope3d_args(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                                     const float* gamma_q, const float* gamma_k,
+                                     int32_t T, int32_t Hl, int32_t Wl, int32_t t0,
+                                     int32_t n_heads, int32_t head_dim,
+                                     int32_t d_t, int32_t d_h, int32_t d_w,
+                                     float theta, float eps);
+int sdit_validate_kv_quant_args(const void* x, const int8_t* codes, const float* scales,
+                                int32_t n_tok, int32_t n_heads, int32_t head_dim);
+int sdit_validate_attn_args(const void* q, int32_t n_q,
+                            const sdit_kv_segment* segs, int32_t n_segs,
+                            const uint8_t* block_mask, int32_t block_q, int32_t block_k,
+                            int32_t n_heads, int32_t head_dim, float softmax_scale,
+                            const void* out, const float* lse);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDIT_H */

@@ -1,0 +1,149 @@
+"""Python binding of the sdit C ABI (include/sdit.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels of libsdit.so. Tensors are passed as device pointers (torch tensors
+or raw integer addresses); the stream defaults to torch's current stream.
+The library is loaded on first use; every call fails loudly (ImportError)
+when the built library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsdit.so")
+
+SDIT_OK, SDIT_ERR_INVALID, SDIT_ERR_UNSUPPORTED, SDIT_ERR_DEVICE = 0, 1, 2, 3
+SDIT_BF16, SDIT_INT8 = 0, 1
+SDIT_MAX_SEGMENTS = 8
+ABI_VERSION = 1
+
+_lib = None
+
+
+class KVSegment(ctypes.Structure):
+    """struct sdit_kv_segment."""
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("len", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_i32, _f32, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libsdit.so (loaded on first use; raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m streaming_video_dit_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.sdit_abi_version.restype = ctypes.c_int
+    L.sdit_status_string.restype = ctypes.c_char_p
+    L.sdit_status_string.argtypes = [ctypes.c_int]
+    L.sdit_last_error.restype = ctypes.c_char_p
+    L.sdit_qknorm_rope3d.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp] + [_i32] * 9 + [_f32, _f32, _vp]
+    L.sdit_validate_qknorm_rope3d_args.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp] + [_i32] * 9 + [_f32, _f32]
+    L.sdit_kv_quant_int8.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _vp]
+    L.sdit_validate_kv_quant_args.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32]
+    L.sdit_attn_fwd.argtypes = [_vp, _i32, ctypes.POINTER(KVSegment), _i32, _vp, _i32, _i32, _i32, _i32, _f32,
+                                _vp, _vp, _vp]
+    L.sdit_validate_attn_args.argtypes = [_vp, _i32, ctypes.POINTER(KVSegment), _i32, _vp, _i32, _i32, _i32,
+                                          _i32, _f32, _vp, _vp]
+    for n in ("sdit_qknorm_rope3d", "sdit_validate_qknorm_rope3d_args", "sdit_kv_quant_int8",
+              "sdit_validate_kv_quant_args", "sdit_attn_fwd", "sdit_validate_attn_args"):
+        getattr(L, n).restype = ctypes.c_int
+    if L.sdit_abi_version() != ABI_VERSION:
+        raise ImportError(f"libsdit.so ABI {L.sdit_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = L
+    return L
+
+
+class SditError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{lib().sdit_status_string(status).decode()}: {message}")
+        self.status = status
+
+
+def last_error() -> str:
+    return lib().sdit_last_error().decode()
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int):
+    if status != SDIT_OK:
+        raise SditError(status, last_error())
+
+
+def qknorm_rope3d(q_in, k_in, q_out, k_out, gamma_q, gamma_k, T: int, Hl: int, Wl: int, t0: int,
+                  n_heads: int, head_dim: int, d_t: int, d_h: int, d_w: int,
+                  theta: float = 1.0e4, eps: float = 1.0e-6, stream=None) -> None:
+    """sdit_qknorm_rope3d."""
+    _check(lib().sdit_qknorm_rope3d(_ptr(q_in), _ptr(k_in), _ptr(q_out), _ptr(k_out), _ptr(gamma_q), _ptr(gamma_k),
+                                   T, Hl, Wl, t0, n_heads, head_dim, d_t, d_h, d_w, theta, eps, _stream(stream)))
+
+
+def kv_quant_int8(x, codes, scales, n_tok: int, n_heads: int, head_dim: int, stream=None) -> None:
+    """sdit_kv_quant_int8."""
+    _check(lib().sdit_kv_quant_int8(_ptr(x), _ptr(codes), _ptr(scales), n_tok, n_heads, head_dim, _stream(stream)))
+
+
+def make_segments(segs: Sequence[dict]):
+    """Host array of sdit_kv_segment from dicts with k, v, len, dtype and
+    (int8) k_scale, v_scale."""
+    arr = (KVSegment * max(1, len(segs)))()
+    for i, s in enumerate(segs):
+        arr[i].k = _ptr(s.get("k"))
+        arr[i].v = _ptr(s.get("v"))
+        arr[i].k_scale = _ptr(s.get("k_scale"))
+        arr[i].v_scale = _ptr(s.get("v_scale"))
+        arr[i].len = int(s["len"])
+        arr[i].dtype = int(s.get("dtype", SDIT_BF16))
+    return arr
+
+
+def attn_fwd(q, n_q: int, segs, block_mask, block_q: int, block_k: int, n_heads: int, head_dim: int,
+             out, lse=None, softmax_scale: float = 0.0, stream=None) -> None:
+    """sdit_attn_fwd. ``segs`` is a list of dicts (see make_segments) or a
+    ctypes array made by make_segments."""
+    arr = segs if isinstance(segs, ctypes.Array) else make_segments(segs)
+    n = len(segs)
+    _check(lib().sdit_attn_fwd(_ptr(q), n_q, arr, n, _ptr(block_mask), block_q, block_k, n_heads, head_dim,
+                              softmax_scale, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def validate_attn_args(q, n_q, segs, block_mask, block_q, block_k, n_heads, head_dim, out, lse=None,
+                       softmax_scale: float = 0.0) -> int:
+    arr = segs if isinstance(segs, ctypes.Array) else make_segments(segs)
+    return lib().sdit_validate_attn_args(_ptr(q), n_q, arr, len(segs), _ptr(block_mask), block_q, block_k, n_heads,
+                                        head_dim, softmax_scale, _ptr(out), _ptr(lse))
+
+
+def validate_qknorm_rope3d_args(q_in, k_in, q_out, k_out, gamma_q, gamma_k, T, Hl, Wl, t0, n_heads, head_dim,
+                                d_t, d_h, d_w, theta=1.0e4, eps=1.0e-6) -> int:
+    return lib().sdit_validate_qknorm_rope3d_args(_ptr(q_in), _ptr(k_in), _ptr(q_out), _ptr(k_out), _ptr(gamma_q),
+                                                 _ptr(gamma_k), T, Hl, Wl, t0, n_heads, head_dim, d_t, d_h, d_w,
+                                                 theta, eps)
+
+
+def validate_kv_quant_args(x, codes, scales, n_tok, n_heads, head_dim) -> int:
+    return lib().sdit_validate_kv_quant_args(_ptr(x), _ptr(codes), _ptr(scales), n_tok, n_heads, head_dim)

@@ -1,0 +1,57 @@
+"""Compile the sdit HIP library for gfx950, in-tree.
+
+    python -m streaming_video_dit_amd.build
+
+writes streaming_video_dit_amd/libsdit.so next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libsdit.so")
+
+SOURCES = ["sdit_api.cpp", "qknorm_rope3d.hip", "kv_quant_int8.hip", "attn_fwd.hip"]
+
+FLAGS = [
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-fvisibility=hidden",
+    # correctly rounded fp32 divide/sqrt (the int8 quantiser depends on it)
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # keep the compiler from forming packed fp32 instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc()] + FLAGS + list(extra_flags or []) + ["-I", os.path.join(ROOT, "include"), "-o", tmp] + srcs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-fp32 feature and says so; anything else is shown
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msgs = [l for l in (r.stdout + r.stderr).splitlines() if noise not in l and l.strip()]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

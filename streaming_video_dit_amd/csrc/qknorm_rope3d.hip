@@ -1,0 +1,142 @@
+// Fused QK-RMSNorm + 3D (t, h, w) rotary embedding, gfx950.
+//
+// The "QK-norm+3D RoPE" operator of the Joy-face_change_optimized README
+// (table of changed files). Per (token, head) row of head_dim bf16 values:
+//   y_c = x_c / sqrt(mean(x^2) + eps) * gamma_c
+// then interleaved pairs (2j, 2j+1) of the axis blocks t | h | w (widths
+// d_t, d_h, d_w) are rotated by p_axis * theta^(-2j/d_axis), and the result
+// is rounded to bf16 once.
+//
+// HBM-bound (2 * 2 * d bytes per row and tensor). Work unit: one token, one
+// tensor (q or k) and a group of up to kHeadsPerUnit heads, handled by d/8
+// lanes that each own 8 consecutive columns (16 B per row, coalesced 256 B
+// rows). A lane's four rotation angles depend only on the token, so they are
+// computed once per unit and reused for every head of the unit. Angles are
+// formed and reduced modulo 2*pi in fp64 and only then handed to sincosf, so
+// the rotation error stays near one binary32 rounding even for the largest
+// positions (w up to ~100 at theta^0).
+#include "sdit_internal.h"
+
+namespace sdit {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kHeadsPerUnit = 4;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo;
+  const __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int UNITS_PER_BLOCK = kThreads / LPR;
+  const int lane_in_row = threadIdx.x % LPR;
+  const int n_hg = (p.n_heads + kHeadsPerUnit - 1) / kHeadsPerUnit;
+  const int64_t unit = (int64_t)blockIdx.x * UNITS_PER_BLOCK + threadIdx.x / LPR;
+  const int64_t n_units = (int64_t)p.n_tok * 2 * n_hg;
+  const bool active = unit < n_units;
+  const int64_t u = active ? unit : 0;
+  const int tok = (int)(u / (2 * n_hg));
+  const int rem = (int)(u % (2 * n_hg));
+  const int is_k = rem / n_hg;
+  const int h0 = (rem % n_hg) * kHeadsPerUnit;
+  const int nh = min(kHeadsPerUnit, p.n_heads - h0);
+
+  const uint16_t* in = is_k ? p.k_in : p.q_in;
+  uint16_t* out = is_k ? p.k_out : p.q_out;
+  const float* gamma = is_k ? p.gamma_k : p.gamma_q;
+  const int c0 = lane_in_row * 8;
+
+  // Issue the row loads first; they are independent of the angle math.
+  uint4 raw[kHeadsPerUnit];
+#pragma unroll
+  for (int i = 0; i < kHeadsPerUnit; ++i) {
+    if (active && i < nh)
+      raw[i] = *reinterpret_cast<const uint4*>(in + ((int64_t)tok * p.n_heads + h0 + i) * D + c0);
+    else
+      raw[i] = make_uint4(0, 0, 0, 0);
+  }
+  const float4 g0 = *reinterpret_cast<const float4*>(gamma + c0);
+  const float4 g1 = *reinterpret_cast<const float4*>(gamma + c0 + 4);
+  const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+
+  // Token position on the three axes.
+  const int HW = p.Hl * p.Wl;
+  const int pos_t = p.t0 + tok / HW;
+  const int pos_h = (tok / p.Wl) % p.Hl;
+  const int pos_w = tok % p.Wl;
+
+  float cs[4], sn[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = c0 + 2 * i;           // first column of the pair
+    int pos, j, da;
+    if (c < p.d_t) {
+      pos = pos_t; j = c / 2; da = p.d_t;
+    } else if (c < p.d_t + p.d_h) {
+      pos = pos_h; j = (c - p.d_t) / 2; da = p.d_h;
+    } else {
+      pos = pos_w; j = (c - p.d_t - p.d_h) / 2; da = p.d_w;
+    }
+    const double omega = exp2(-2.0 * (double)j / (double)da * p.log2_theta);
+    double phi = (double)pos * omega;
+    const double two_pi = 6.283185307179586476925286766559;
+    phi -= two_pi * rint(phi / two_pi);  // |phi| <= pi
+    sincosf((float)phi, &sn[i], &cs[i]);
+  }
+
+#pragma unroll
+  for (int i = 0; i < kHeadsPerUnit; ++i) {
+    float x[8];
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_lo(w[e]);
+      x[2 * e + 1] = bf16_hi(w[e]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    const float inv = 1.0f / sqrtf(ss / (float)D + p.eps);
+
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float y0 = x[2 * e] * inv * g[2 * e];
+      const float y1 = x[2 * e + 1] * inv * g[2 * e + 1];
+      const float r0 = y0 * cs[e] - y1 * sn[e];
+      const float r1 = y0 * sn[e] + y1 * cs[e];
+      o[e] = pack_bf16x2(r0, r1);
+    }
+    if (active && i < nh)
+      *reinterpret_cast<uint4*>(out + ((int64_t)tok * p.n_heads + h0 + i) * D + c0) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+template <int D>
+hipError_t launch(const RopeParams& p, hipStream_t stream) {
+  constexpr int UNITS_PER_BLOCK = kThreads / (D / 8);
+  const int n_hg = (p.n_heads + kHeadsPerUnit - 1) / kHeadsPerUnit;
+  const int64_t n_units = (int64_t)p.n_tok * 2 * n_hg;
+  const int64_t blocks = (n_units + UNITS_PER_BLOCK - 1) / UNITS_PER_BLOCK;
+  hipLaunchKernelGGL(qknorm_rope3d_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qknorm_rope3d(const RopeParams& p, int head_dim, hipStream_t stream) {
+  if (p.n_tok == 0) return hipSuccess;
+  return head_dim == 128 ? launch<128>(p, stream) : launch<64>(p, stream);
+}
+
+}  // namespace sdit

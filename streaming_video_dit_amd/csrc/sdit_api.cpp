@@ -1,0 +1,275 @@
+// C ABI of the sdit library: argument validation, launch geometry, errors.
+// Every check runs on the host before a launch; nothing here allocates.
+#include "../../include/sdit.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sdit_internal.h"
+
+#define SDIT_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SDIT_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (na <= 0 || nb <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+int device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  if (e == hipErrorNoBinaryForGpu || e == hipErrorInvalidDeviceFunction || e == hipErrorInvalidImage ||
+      e == hipErrorSharedObjectInitFailed)
+    return fail(SDIT_ERR_UNSUPPORTED, "%s: no gfx950 code object for the current device (%s)", what,
+                hipGetErrorString(e));
+  return fail(SDIT_ERR_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+bool valid_block(int b) { return b == 16 || b == 32 || b == 64 || b == 128; }
+
+}  // namespace
+
+SDIT_API int sdit_abi_version(void) { return SDIT_ABI_VERSION; }
+
+SDIT_API const char* sdit_status_string(int status) {
+  switch (status) {
+    case SDIT_OK: return "SDIT_OK";
+    case SDIT_ERR_INVALID: return "SDIT_ERR_INVALID";
+    case SDIT_ERR_UNSUPPORTED: return "SDIT_ERR_UNSUPPORTED";
+    case SDIT_ERR_DEVICE: return "SDIT_ERR_DEVICE";
+    default: return "SDIT_UNKNOWN_STATUS";
+  }
+}
+
+SDIT_API const char* sdit_last_error(void) { return g_err; }
+
+// ------------------------------------------------------------------ qknorm_rope3d
+
+SDIT_API int sdit_validate_qknorm_rope3d_args(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                                              const float* gamma_q, const float* gamma_k, int32_t T,
+                                              int32_t Hl, int32_t Wl, int32_t t0, int32_t n_heads,
+                                              int32_t head_dim, int32_t d_t, int32_t d_h, int32_t d_w,
+                                              float theta, float eps) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SDIT_ERR_UNSUPPORTED, "qknorm_rope3d: head_dim %d not in {64, 128}", head_dim);
+  if (n_heads < 1) return fail(SDIT_ERR_INVALID, "qknorm_rope3d: n_heads %d < 1", n_heads);
+  if (T < 0 || Hl < 0 || Wl < 0 || t0 < 0)
+    return fail(SDIT_ERR_INVALID, "qknorm_rope3d: negative grid (T=%d Hl=%d Wl=%d t0=%d)", T, Hl, Wl, t0);
+  if (d_t < 0 || d_h < 0 || d_w < 0 || (d_t | d_h | d_w) & 1 || d_t + d_h + d_w != head_dim)
+    return fail(SDIT_ERR_INVALID, "qknorm_rope3d: axis split %d/%d/%d must be even and sum to %d", d_t, d_h,
+                d_w, head_dim);
+  if (!(theta > 0.f) || !isfinite(theta)) return fail(SDIT_ERR_INVALID, "qknorm_rope3d: theta must be > 0");
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(SDIT_ERR_INVALID, "qknorm_rope3d: eps must be >= 0");
+  const int64_t n_tok = (int64_t)T * Hl * Wl;
+  if (n_tok > INT32_MAX) return fail(SDIT_ERR_INVALID, "qknorm_rope3d: too many tokens");
+  if ((int64_t)t0 + T > (1 << 24)) return fail(SDIT_ERR_INVALID, "qknorm_rope3d: t positions too large");
+  if (n_tok == 0) return ok();
+  const void* ptrs[4] = {q_in, k_in, q_out, k_out};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned(p, 16))
+      return fail(SDIT_ERR_INVALID, "qknorm_rope3d: q/k pointers must be non-NULL and 16-byte aligned");
+  if (gamma_q == nullptr || gamma_k == nullptr || !aligned(gamma_q, 16) || !aligned(gamma_k, 16))
+    return fail(SDIT_ERR_INVALID, "qknorm_rope3d: gamma pointers must be non-NULL and 16-byte aligned");
+  const int64_t bytes = n_tok * n_heads * head_dim * 2;
+  if ((q_out != q_in && overlap(q_out, bytes, q_in, bytes)) || (k_out != k_in && overlap(k_out, bytes, k_in, bytes)) ||
+      overlap(q_out, bytes, k_out, bytes) || overlap(q_out, bytes, k_in, bytes) || overlap(k_out, bytes, q_in, bytes))
+    return fail(SDIT_ERR_INVALID, "qknorm_rope3d: outputs overlap inputs (only exact in-place is allowed)");
+  if (overlap(q_out, bytes, gamma_q, head_dim * 4) || overlap(q_out, bytes, gamma_k, head_dim * 4) ||
+      overlap(k_out, bytes, gamma_q, head_dim * 4) || overlap(k_out, bytes, gamma_k, head_dim * 4))
+    return fail(SDIT_ERR_INVALID, "qknorm_rope3d: outputs overlap gamma");
+  return ok();
+}
+
+SDIT_API int sdit_qknorm_rope3d(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                                const float* gamma_q, const float* gamma_k, int32_t T, int32_t Hl, int32_t Wl,
+                                int32_t t0, int32_t n_heads, int32_t head_dim, int32_t d_t, int32_t d_h,
+                                int32_t d_w, float theta, float eps, void* stream) {
+  int st = sdit_validate_qknorm_rope3d_args(q_in, k_in, q_out, k_out, gamma_q, gamma_k, T, Hl, Wl, t0, n_heads,
+                                            head_dim, d_t, d_h, d_w, theta, eps);
+  if (st != SDIT_OK) return st;
+  sdit::RopeParams p;
+  p.q_in = (const uint16_t*)q_in;
+  p.k_in = (const uint16_t*)k_in;
+  p.q_out = (uint16_t*)q_out;
+  p.k_out = (uint16_t*)k_out;
+  p.gamma_q = gamma_q;
+  p.gamma_k = gamma_k;
+  p.n_tok = T * Hl * Wl;
+  p.Hl = Hl;
+  p.Wl = Wl;
+  p.t0 = t0;
+  p.n_heads = n_heads;
+  p.d_t = d_t;
+  p.d_h = d_h;
+  p.d_w = d_w;
+  p.log2_theta = log2((double)theta);
+  p.eps = eps;
+  if (p.n_tok == 0) return ok();
+  return device_status(sdit::launch_qknorm_rope3d(p, head_dim, (hipStream_t)stream), "qknorm_rope3d");
+}
+
+// ------------------------------------------------------------------ kv_quant_int8
+
+SDIT_API int sdit_validate_kv_quant_args(const void* x, const int8_t* codes, const float* scales, int32_t n_tok,
+                                         int32_t n_heads, int32_t head_dim) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SDIT_ERR_UNSUPPORTED, "kv_quant_int8: head_dim %d not in {64, 128}", head_dim);
+  if (n_heads < 1 || n_tok < 0) return fail(SDIT_ERR_INVALID, "kv_quant_int8: bad n_tok %d / n_heads %d", n_tok, n_heads);
+  if (n_tok == 0) return ok();
+  if (x == nullptr || codes == nullptr || scales == nullptr)
+    return fail(SDIT_ERR_INVALID, "kv_quant_int8: NULL pointer");
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return fail(SDIT_ERR_INVALID, "kv_quant_int8: x/codes must be 16-byte and scales 4-byte aligned");
+  const int64_t rows = (int64_t)n_tok * n_heads;
+  if (overlap(codes, rows * head_dim, x, rows * head_dim * 2) || overlap(scales, rows * 4, x, rows * head_dim * 2) ||
+      overlap(scales, rows * 4, codes, rows * head_dim))
+    return fail(SDIT_ERR_INVALID, "kv_quant_int8: buffers overlap");
+  return ok();
+}
+
+SDIT_API int sdit_kv_quant_int8(const void* x, int8_t* codes, float* scales, int32_t n_tok, int32_t n_heads,
+                                int32_t head_dim, void* stream) {
+  int st = sdit_validate_kv_quant_args(x, codes, scales, n_tok, n_heads, head_dim);
+  if (st != SDIT_OK) return st;
+  if (n_tok == 0) return ok();
+  sdit::QuantParams p;
+  p.x = (const uint16_t*)x;
+  p.codes = codes;
+  p.scales = scales;
+  p.n_rows = (int64_t)n_tok * n_heads;
+  return device_status(sdit::launch_kv_quant_int8(p, head_dim, (hipStream_t)stream), "kv_quant_int8");
+}
+
+// ------------------------------------------------------------------ attn_fwd
+
+namespace {
+
+int fill_attn_params(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs,
+                     const uint8_t* block_mask, int32_t block_q, int32_t block_k, int32_t n_heads,
+                     int32_t head_dim, float softmax_scale, const void* out, const float* lse,
+                     sdit::AttnParams* P) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SDIT_ERR_UNSUPPORTED, "attn_fwd: head_dim %d not in {64, 128}", head_dim);
+  if (n_heads < 1) return fail(SDIT_ERR_INVALID, "attn_fwd: n_heads %d < 1", n_heads);
+  if (n_q < 0) return fail(SDIT_ERR_INVALID, "attn_fwd: n_q %d < 0", n_q);
+  if (!valid_block(block_q) || !valid_block(block_k))
+    return fail(SDIT_ERR_UNSUPPORTED, "attn_fwd: block sizes %d x %d not in {16, 32, 64, 128}", block_q, block_k);
+  if (n_segs < 1 || n_segs > SDIT_MAX_SEGMENTS)
+    return fail(SDIT_ERR_INVALID, "attn_fwd: n_segs %d not in [1, %d]", n_segs, SDIT_MAX_SEGMENTS);
+  if (segs == nullptr) return fail(SDIT_ERR_INVALID, "attn_fwd: segs is NULL");
+  if (!isfinite(softmax_scale)) return fail(SDIT_ERR_INVALID, "attn_fwd: softmax_scale not finite");
+  if ((int64_t)n_q * n_heads * head_dim > ((int64_t)1 << 40)) return fail(SDIT_ERR_INVALID, "attn_fwd: q too large");
+  int64_t tiles = 0, kbs = 0;
+  for (int s = 0; s < n_segs; ++s) {
+    const sdit_kv_segment& sg = segs[s];
+    if (sg.len < 0) return fail(SDIT_ERR_INVALID, "attn_fwd: segment %d has len %d < 0", s, sg.len);
+    if (sg.dtype != SDIT_BF16 && sg.dtype != SDIT_INT8)
+      return fail(SDIT_ERR_INVALID, "attn_fwd: segment %d has unknown dtype %d", s, sg.dtype);
+    if (sg.dtype == SDIT_BF16 && (sg.k_scale != nullptr || sg.v_scale != nullptr))
+      return fail(SDIT_ERR_INVALID, "attn_fwd: bf16 segment %d must have NULL scales", s);
+    if (sg.len > 0) {
+      if (sg.k == nullptr || sg.v == nullptr || !aligned(sg.k, 16) || !aligned(sg.v, 16))
+        return fail(SDIT_ERR_INVALID, "attn_fwd: segment %d k/v must be non-NULL and 16-byte aligned", s);
+      if (sg.dtype == SDIT_INT8 && (sg.k_scale == nullptr || sg.v_scale == nullptr || !aligned(sg.k_scale, 4) ||
+                                    !aligned(sg.v_scale, 4)))
+        return fail(SDIT_ERR_INVALID, "attn_fwd: int8 segment %d needs 4-byte aligned k_scale and v_scale", s);
+      const int64_t esz = sg.dtype == SDIT_INT8 ? 1 : 2;
+      const int64_t seg_bytes = (int64_t)sg.len * n_heads * head_dim * esz;
+      const int64_t out_bytes = (int64_t)n_q * n_heads * head_dim * 2;
+      if (overlap(out, out_bytes, sg.k, seg_bytes) || overlap(out, out_bytes, sg.v, seg_bytes))
+        return fail(SDIT_ERR_INVALID, "attn_fwd: out overlaps segment %d", s);
+    }
+    tiles += (sg.len + sdit::kAttnBK - 1) / sdit::kAttnBK;
+    kbs += ceil_div(sg.len, block_k);
+  }
+  if (tiles > (1 << 24)) return fail(SDIT_ERR_UNSUPPORTED, "attn_fwd: more than 2^30 keys");
+  const int n_qb = ceil_div(n_q, block_q);
+  const int n_qt = ceil_div(n_q, sdit::kAttnBQ);
+  if ((int64_t)n_qt * n_heads > INT32_MAX / 2) return fail(SDIT_ERR_INVALID, "attn_fwd: grid too large");
+  if (n_q > 0) {
+    if (q == nullptr || !aligned(q, 16)) return fail(SDIT_ERR_INVALID, "attn_fwd: q must be non-NULL, 16-byte aligned");
+    if (out == nullptr || !aligned(out, 16))
+      return fail(SDIT_ERR_INVALID, "attn_fwd: out must be non-NULL, 16-byte aligned");
+    if (lse != nullptr && !aligned(lse, 4)) return fail(SDIT_ERR_INVALID, "attn_fwd: lse must be 4-byte aligned");
+    if (kbs > 0 && block_mask == nullptr) return fail(SDIT_ERR_INVALID, "attn_fwd: block_mask is NULL");
+    const int64_t qbytes = (int64_t)n_q * n_heads * head_dim * 2;
+    if (overlap(out, qbytes, q, qbytes)) return fail(SDIT_ERR_INVALID, "attn_fwd: out overlaps q");
+    if (lse != nullptr && (overlap(lse, (int64_t)n_q * n_heads * 4, out, qbytes) ||
+                           overlap(lse, (int64_t)n_q * n_heads * 4, q, qbytes)))
+      return fail(SDIT_ERR_INVALID, "attn_fwd: lse overlaps q or out");
+  }
+  if (P != nullptr) {
+    memset(P, 0, sizeof(*P));
+    P->q = (const uint16_t*)q;
+    P->out = (uint16_t*)out;
+    P->lse = (float*)lse;
+    P->mask = block_mask;
+    int tile = 0, kb = 0;
+    for (int s = 0; s < n_segs; ++s) {
+      P->seg[s].k = segs[s].k;
+      P->seg[s].v = segs[s].v;
+      P->seg[s].k_scale = segs[s].k_scale;
+      P->seg[s].v_scale = segs[s].v_scale;
+      P->seg[s].len = segs[s].len;
+      P->seg[s].is_int8 = segs[s].dtype == SDIT_INT8;
+      P->seg[s].tile_start = tile;
+      P->seg[s].kb_start = kb;
+      tile += ceil_div(segs[s].len, sdit::kAttnBK);
+      kb += ceil_div(segs[s].len, block_k);
+    }
+    P->n_segs = n_segs;
+    P->n_q = n_q;
+    P->n_heads = n_heads;
+    P->n_qt = n_qt;
+    P->n_tiles = tile;
+    P->n_kb = kb;
+    P->n_qb = n_qb;
+    P->block_q = block_q;
+    P->block_k = block_k;
+    const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / sqrt((double)head_dim);
+    P->scale_log2 = (float)(scale * 1.4426950408889634073599246810019);
+  }
+  return ok();
+}
+
+}  // namespace
+
+SDIT_API int sdit_validate_attn_args(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs,
+                                     const uint8_t* block_mask, int32_t block_q, int32_t block_k, int32_t n_heads,
+                                     int32_t head_dim, float softmax_scale, const void* out, const float* lse) {
+  return fill_attn_params(q, n_q, segs, n_segs, block_mask, block_q, block_k, n_heads, head_dim, softmax_scale, out,
+                          lse, nullptr);
+}
+
+SDIT_API int sdit_attn_fwd(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs,
+                           const uint8_t* block_mask, int32_t block_q, int32_t block_k, int32_t n_heads,
+                           int32_t head_dim, float softmax_scale, void* out, float* lse, void* stream) {
+  sdit::AttnParams P;
+  int st = fill_attn_params(q, n_q, segs, n_segs, block_mask, block_q, block_k, n_heads, head_dim, softmax_scale,
+                            out, lse, &P);
+  if (st != SDIT_OK) return st;
+  if (n_q == 0) return ok();
+  return device_status(sdit::launch_attn_fwd(P, head_dim, (hipStream_t)stream), "attn_fwd");
+}

@@ -1,0 +1,68 @@
+// Internal declarations shared by the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdit {
+
+constexpr int kMaxSegments = 8;
+
+// ---------------------------------------------------------------- qknorm_rope3d
+struct RopeParams {
+  const uint16_t* q_in;
+  const uint16_t* k_in;
+  uint16_t* q_out;
+  uint16_t* k_out;
+  const float* gamma_q;
+  const float* gamma_k;
+  int32_t n_tok, Hl, Wl, t0;
+  int32_t n_heads, d_t, d_h, d_w;
+  double log2_theta;   // log2(theta), computed on the host in double
+  float eps;
+};
+hipError_t launch_qknorm_rope3d(const RopeParams& p, int head_dim, hipStream_t stream);
+
+// ---------------------------------------------------------------- kv_quant_int8
+struct QuantParams {
+  const uint16_t* x;
+  int8_t* codes;
+  float* scales;
+  int64_t n_rows;      // n_tok * n_heads
+};
+hipError_t launch_kv_quant_int8(const QuantParams& p, int head_dim, hipStream_t stream);
+
+// ---------------------------------------------------------------- attn_fwd
+struct AttnSegment {
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t len;
+  int32_t is_int8;
+  int32_t tile_start;  // first 64-key tile of this segment in the global tile numbering
+  int32_t kb_start;    // first mask column (k-block) of this segment
+};
+
+struct AttnParams {
+  const uint16_t* q;
+  uint16_t* out;
+  float* lse;
+  const uint8_t* mask;
+  AttnSegment seg[kMaxSegments];
+  int32_t n_segs;
+  int32_t n_q;
+  int32_t n_heads;
+  int32_t n_qt;        // 128-row query tiles
+  int32_t n_tiles;     // total 64-key tiles over all segments
+  int32_t n_kb;        // mask columns
+  int32_t n_qb;        // mask rows
+  int32_t block_q;
+  int32_t block_k;
+  float scale_log2;    // softmax_scale * log2(e)
+};
+constexpr int kAttnBQ = 128;  // query rows per workgroup
+constexpr int kAttnBK = 64;   // keys per pipeline stage
+hipError_t launch_attn_fwd(const AttnParams& p, int head_dim, hipStream_t stream);
+
+}  // namespace sdit

@@ -1,0 +1,130 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function
+include/sdit.h declares, and the host-side validators reject bad arguments
+with the documented status (nothing is launched by a validator)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import streaming_video_dit_amd as sdit
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdit.h")
+
+A16 = 0x10000          # fake, 16-byte aligned device addresses (never dereferenced)
+MB = 1 << 20
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdit_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = _declared_functions()
+    assert "sdit_attn_fwd" in names and "sdit_kv_quant_int8" in names and "sdit_qknorm_rope3d" in names
+    L = sdit.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    L = sdit.lib()
+    assert L.sdit_abi_version() == sdit.ABI_VERSION == 1
+    assert L.sdit_status_string(0) == b"SDIT_OK"
+    assert L.sdit_status_string(2) == b"SDIT_ERR_UNSUPPORTED"
+    assert ctypes.sizeof(sdit.KVSegment) == 40
+
+
+def _rope_args(**kw):
+    a = dict(q_in=A16, k_in=A16 + 16 * MB, q_out=A16 + 32 * MB, k_out=A16 + 48 * MB, gamma_q=A16 + 64 * MB,
+             gamma_k=A16 + 65 * MB, T=3, Hl=30, Wl=52, t0=9, n_heads=12, head_dim=128, d_t=44, d_h=42, d_w=42)
+    a.update(kw)
+    return a
+
+
+def test_qknorm_validation():
+    v = lambda **kw: sdit.validate_qknorm_rope3d_args(**_rope_args(**kw))
+    assert v() == sdit.SDIT_OK
+    assert v(q_out=A16, k_out=A16 + 16 * MB) == sdit.SDIT_OK              # exact in place
+    assert v(head_dim=96, d_t=32, d_h=32, d_w=32) == sdit.SDIT_ERR_UNSUPPORTED
+    assert v(d_t=43, d_h=43) == sdit.SDIT_ERR_INVALID                      # odd widths
+    assert v(d_t=40) == sdit.SDIT_ERR_INVALID                              # does not sum to d
+    assert v(q_in=A16 + 4) == sdit.SDIT_ERR_INVALID                        # misaligned
+    assert v(k_in=None) == sdit.SDIT_ERR_INVALID
+    assert v(q_out=A16 + 1024) == sdit.SDIT_ERR_INVALID                    # partial overlap
+    assert v(n_heads=0) == sdit.SDIT_ERR_INVALID
+    assert v(T=0, q_in=None) == sdit.SDIT_OK                               # empty grid: no-op
+    assert v(theta=0.0) == sdit.SDIT_ERR_INVALID
+    assert "axis split" in (v(d_t=40), sdit.last_error())[1]
+
+
+def test_kv_quant_validation():
+    v = sdit.validate_kv_quant_args
+    assert v(A16, A16 + 16 * MB, A16 + 32 * MB, 100, 12, 128) == sdit.SDIT_OK
+    assert v(A16, A16 + 16 * MB, A16 + 32 * MB, 100, 12, 80) == sdit.SDIT_ERR_UNSUPPORTED
+    assert v(A16, A16 + 8, A16 + 32 * MB, 100, 12, 128) == sdit.SDIT_ERR_INVALID
+    assert v(A16, A16 + 1024, A16 + 32 * MB, 100, 12, 128) == sdit.SDIT_ERR_INVALID   # overlap
+    assert v(None, None, None, 0, 12, 128) == sdit.SDIT_OK
+    assert v(A16, A16 + 16 * MB, A16 + 32 * MB + 2, 100, 12, 128) == sdit.SDIT_ERR_INVALID
+
+
+def _segs(n=3, **kw):
+    base = [dict(k=A16 + (1 + 2 * i) * 64 * MB, v=A16 + (2 + 2 * i) * 64 * MB, len=100 + i, dtype=sdit.SDIT_BF16)
+            for i in range(n)]
+    for i, s in kw.items():
+        base[int(i[1:])].update(s)
+    return base
+
+
+def test_attn_validation():
+    q, out, mask = A16, A16 + 1000 * MB, A16 + 2000 * MB
+
+    def v(segs=None, **kw):
+        a = dict(q=q, n_q=300, segs=_segs() if segs is None else segs, block_mask=mask, block_q=128, block_k=128,
+                 n_heads=12, head_dim=128, out=out, lse=None)
+        a.update(kw)
+        return sdit.validate_attn_args(**a)
+
+    assert v() == sdit.SDIT_OK
+    assert v(lse=A16 + 3000 * MB) == sdit.SDIT_OK
+    assert v(block_q=48) == sdit.SDIT_ERR_UNSUPPORTED
+    assert v(head_dim=256) == sdit.SDIT_ERR_UNSUPPORTED
+    assert v(segs=_segs(9)) == sdit.SDIT_ERR_INVALID
+    assert v(segs=[]) == sdit.SDIT_ERR_INVALID
+    assert v(segs=_segs(s1=dict(dtype=sdit.SDIT_INT8))) == sdit.SDIT_ERR_INVALID           # int8 without scales
+    assert v(segs=_segs(s1=dict(dtype=sdit.SDIT_INT8, k_scale=A16 + 4000 * MB,
+                                v_scale=A16 + 4001 * MB))) == sdit.SDIT_OK
+    assert v(segs=_segs(s0=dict(k_scale=A16 + 4000 * MB))) == sdit.SDIT_ERR_INVALID        # bf16 with scale
+    assert v(segs=_segs(s2=dict(dtype=7))) == sdit.SDIT_ERR_INVALID
+    assert v(segs=_segs(s2=dict(len=-1))) == sdit.SDIT_ERR_INVALID
+    assert v(segs=_segs(s2=dict(len=0, k=None, v=None))) == sdit.SDIT_OK                   # empty segment
+    assert v(segs=_segs(s0=dict(k=A16 + 8))) == sdit.SDIT_ERR_INVALID                      # misaligned
+    assert v(block_mask=None) == sdit.SDIT_ERR_INVALID
+    assert v(out=q + 4096) == sdit.SDIT_ERR_INVALID                                       # out overlaps q
+    assert v(out=_segs()[1]["k"] + 256) == sdit.SDIT_ERR_INVALID                          # out overlaps K
+    assert v(lse=A16 + 3000 * MB + 2) == sdit.SDIT_ERR_INVALID
+    assert v(n_q=0, q=None, out=None, block_mask=None) == sdit.SDIT_OK
+    assert v(n_q=-1) == sdit.SDIT_ERR_INVALID
+    assert v(n_heads=0) == sdit.SDIT_ERR_INVALID
+    assert v(softmax_scale=float("nan")) == sdit.SDIT_ERR_INVALID
+    assert "segment 1" in (v(segs=_segs(s1=dict(dtype=sdit.SDIT_INT8))), sdit.last_error())[1]
+
+
+def test_error_message_is_per_call():
+    sdit.validate_kv_quant_args(A16, A16 + 8, A16 + 32 * MB, 100, 12, 128)
+    assert sdit.last_error() != ""
+    sdit.validate_kv_quant_args(A16, A16 + 16 * MB, A16 + 32 * MB, 100, 12, 128)
+    assert sdit.last_error() == ""
+
+
+def test_product_path_does_not_touch_the_oracle():
+    import sys
+    import subprocess
+    code = ("import sys, streaming_video_dit_amd as s; s.lib(); "
+            "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules), sorted(sys.modules)")
+    subprocess.run([sys.executable, "-c", code], check=True, cwd=ROOT)
+    src = open(os.path.join(ROOT, "streaming_video_dit_amd", "__init__.py")).read()
+    assert "oracle" not in src.replace("oracle-free", "")

@@ -1,0 +1,305 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Bars: int8 codes and fp32 scales bit-exact; qknorm_rope3d within one bf16
+ulp of the oracle's single rounding; attention within max-abs 4e-3 and
+relative RMS 1e-2 of the unrounded fp64 result, LSE within 1e-3.
+Small cases are compared element by element; the full-size workloads run in
+the same launch configuration as the benchmark and are compared on sampled
+query rows (every head, first/last/ragged q-tiles)."""
+import numpy as np
+import pytest
+
+import workloads as W
+from helpers import (assert_attn_close, dev, empty_bf16, gpu_segments, host_u16, ordered, run_attn,
+                     segments_for_oracle)
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ kv_quant_int8
+
+def _gpu_quant(x_bits):
+    import torch
+    import streaming_video_dit_amd as sdit
+    n, H, d = x_bits.shape
+    x = dev(x_bits)
+    codes = torch.full((n, H, d), 99, dtype=torch.int8, device="cuda")
+    scales = torch.full((n, H), float("nan"), dtype=torch.float32, device="cuda")
+    sdit.kv_quant_int8(x, codes, scales, n, H, d)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
+def test_kv_quant_bit_exact_on_the_int8_cache_workload():
+    cfg = W.CONFIGS["wan13b_int8"]
+    inp = W.make_inputs(cfg)
+    for name, x in [("text K", inp.cache_k[0]), ("text V", inp.cache_v[0]),
+                    ("history K", inp.cache_k[1]), ("history V", inp.cache_v[1]), ("chunk K", inp.k)]:
+        _say("kv_quant", name, x.shape)
+        c, s = _gpu_quant(x)
+        rc, rs = oracle.kv_quant_int8(x)
+        assert np.array_equal(s.view(np.uint32), rs.view(np.uint32)), name
+        assert np.array_equal(c, rc), f"{name}: {(c != rc).sum()} codes differ"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_tok,H", [(1, 1), (3, 5), (1000, 12)])
+def test_kv_quant_edge_cases(d, n_tok, H):
+    rng = np.random.default_rng(n_tok * 7 + d)
+    x = W.normal_bf16(n_tok + d, 1, (n_tok, H, d), outlier_p=0.05, outlier_tid=2)
+    x[0, 0, :] = 0                                   # all-zero row
+    if n_tok > 1:
+        x[1, 0, :] = 0
+        x[1, 0, d // 2] = 0xBF80                     # single nonzero (-1.0)
+    if n_tok > 2:
+        # amax = 127 * 2^-3 makes the scale a power of two: exact half-way quotients
+        vals = (np.arange(d) - d // 2 + 0.5).astype(np.float32) * np.float32(0.125)
+        vals[0] = 127 * 0.125
+        x[2, H - 1, :] = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    _say("kv_quant edge", d, n_tok, H)
+    c, s = _gpu_quant(x)
+    rc, rs = oracle.kv_quant_int8(x)
+    assert np.array_equal(s.view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(c, rc)
+
+
+# ------------------------------------------------------------------ qknorm_rope3d
+
+def _gpu_rope(cfg_like, q_bits, k_bits, gq, gk, in_place=False):
+    import torch
+    import streaming_video_dit_amd as sdit
+    T, Hl, Wl, t0, (dt, dh, dw) = cfg_like
+    n, H, d = q_bits.shape
+    qi, ki = dev(q_bits), dev(k_bits)
+    qo, ko = (qi, ki) if in_place else (empty_bf16((n, H, d)), empty_bf16((n, H, d)))
+    sdit.qknorm_rope3d(qi, ki, qo, ko, dev(gq), dev(gk), T, Hl, Wl, t0, H, d, dt, dh, dw, 1.0e4, 1.0e-6)
+    torch.cuda.synchronize()
+    return host_u16(qo), host_u16(ko)
+
+
+def _check_rope(got, x_bits, g, geo):
+    T, Hl, Wl, t0, (dt, dh, dw) = geo
+    ref = oracle.qknorm_rope3d(x_bits, g, T, Hl, Wl, t0, dt, dh, dw)
+    ulps = np.abs(ordered(got) - ordered(ref))
+    same = float((ulps == 0).mean())
+    _say(f"   max ulp {int(ulps.max())}, identical {100 * same:.4f}%")
+    assert ulps.max() <= 1
+    assert same >= 0.999
+    return same
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan13b", "large_dit"])
+def test_qknorm_rope3d_within_one_ulp(name):
+    cfg = W.CONFIGS[name]
+    inp = W.make_inputs(cfg)
+    geo = (cfg.T, cfg.Hl, cfg.Wl, cfg.t0, cfg.split)
+    _say("qknorm_rope3d", name, inp.q.shape)
+    gq, gk = _gpu_rope(geo, inp.q, inp.k, inp.gamma_q, inp.gamma_k)
+    _check_rope(gq, inp.q, inp.gamma_q, geo)
+    _check_rope(gk, inp.k, inp.gamma_k, geo)
+
+
+def test_qknorm_rope3d_in_place_equals_out_of_place():
+    cfg = W.CONFIGS["wan13b"]
+    inp = W.make_inputs(cfg, n_heads=3)
+    geo = (cfg.T, cfg.Hl, cfg.Wl, cfg.t0, cfg.split)
+    a = _gpu_rope(geo, inp.q, inp.k, inp.gamma_q, inp.gamma_k)
+    b = _gpu_rope(geo, inp.q, inp.k, inp.gamma_q, inp.gamma_k, in_place=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("split,d", [((64, 0, 0), 64), ((0, 0, 64), 64), ((20, 24, 20), 64), ((0, 128, 0), 128)])
+def test_qknorm_rope3d_other_splits(split, d):
+    geo = (2, 3, 5, 7, split)
+    n, H = 2 * 3 * 5, 3
+    q = W.normal_bf16(31, 0, (n, H, d))
+    k = W.normal_bf16(31, 1, (n, H, d))
+    gq = W.uniform_f32(31, 2, (d,), 0.5, 1.5)
+    gk = W.uniform_f32(31, 3, (d,), 0.5, 1.5)
+    a, b = _gpu_rope(geo, q, k, gq, gk)
+    _check_rope(a, q, gq, geo)
+    _check_rope(b, k, gk, geo)
+
+
+# ------------------------------------------------------------------ attention: tiny workload end to end
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_dense"])
+def test_tiny_workload_end_to_end(name):
+    cfg = W.CONFIGS[name]
+    inp = W.make_inputs(cfg)
+    geo = (cfg.T, cfg.Hl, cfg.Wl, cfg.t0, cfg.split)
+    _say("tiny end to end", name)
+    gq, gk = _gpu_rope(geo, inp.q, inp.k, inp.gamma_q, inp.gamma_k)
+    dt, dh, dw = cfg.split
+    rq = oracle.qknorm_rope3d(inp.q, inp.gamma_q, cfg.T, cfg.Hl, cfg.Wl, cfg.t0, dt, dh, dw)
+    rk = oracle.qknorm_rope3d(inp.k, inp.gamma_k, cfg.T, cfg.Hl, cfg.Wl, cfg.t0, dt, dh, dw)
+    assert np.abs(ordered(gq) - ordered(rq)).max() <= 1
+    # each side runs its own chain: GPU rope -> GPU attention, oracle rope -> oracle attention
+    out, lse = run_attn(gq, segments_for_oracle(inp, gk), inp.mask, cfg.block, cfg.block)
+    O, LSE = oracle.attention(rq, segments_for_oracle(inp, rk), inp.mask, cfg.block, cfg.block)
+    e = assert_attn_close(out, lse, O, LSE, name)
+    _say(f"   max-abs {e[0]:.2e}, rel-RMS {e[1]:.2e}")
+
+
+def test_tiny_mask_readings_differ_on_gpu():
+    cfg = W.CONFIGS["tiny"]
+    inp = W.make_inputs(cfg)
+    segs = segments_for_oracle(inp, inp.k)
+    a, _ = run_attn(inp.q, segs, W.make_mask(cfg), 16, 16)
+    b, _ = run_attn(inp.q, segs, W.make_mask(W.CONFIGS["tiny_dense"]), 16, 16)
+    assert np.array_equal(a[16:], b[16:])
+    assert not np.array_equal(a[:16], b[:16])
+
+
+# ------------------------------------------------------------------ attention: small cases, every element
+
+def _rand_case(seed, n_q, H, d, lens, dtypes, bq, bk, density=1.0, empty_rows=()):
+    q = W.normal_bf16(seed, 0, (n_q, H, d))
+    segs = []
+    for i, (L, dt) in enumerate(zip(lens, dtypes)):
+        k = W.normal_bf16(seed, 10 + 2 * i, (L, H, d), outlier_p=0.01, outlier_tid=50 + i)
+        v = W.normal_bf16(seed, 11 + 2 * i, (L, H, d), outlier_p=0.01, outlier_tid=60 + i)
+        if dt == "int8":
+            ck, sk = oracle.kv_quant_int8(k)
+            cv, sv = oracle.kv_quant_int8(v)
+            segs.append({"k": ck, "v": cv, "k_scale": sk, "v_scale": sv, "dtype": "int8"})
+        else:
+            segs.append({"k": k, "v": v, "dtype": "bf16"})
+    nqb = -(-n_q // bq)
+    nkb = sum(-(-L // bk) for L in lens)
+    rng = np.random.default_rng([seed, 100])
+    mask = (rng.random((nqb, nkb)) < density).astype(np.uint8)
+    for r in empty_rows:
+        mask[r] = 0
+    return q, segs, mask
+
+
+CASES = {
+    # name: (n_q, H, d, segment lengths, dtypes, block_q, block_k, density, empty q-block rows)
+    "d128_ragged_3seg": (300, 2, 128, [77, 300, 130], ["bf16"] * 3, 128, 128, 1.0, ()),
+    "d128_int8_mix": (257, 3, 128, [64, 200, 257], ["int8", "int8", "bf16"], 128, 128, 1.0, ()),
+    "d128_sparse": (640, 2, 128, [640], ["bf16"], 128, 128, 0.35, (2,)),
+    "d128_small_blocks": (200, 2, 128, [50, 150, 200], ["bf16", "int8", "bf16"], 32, 16, 0.6, (0,)),
+    "d64_b64": (190, 2, 64, [33, 190], ["bf16", "bf16"], 64, 64, 0.7, ()),
+    "d64_b32_int8": (100, 1, 64, [129, 100], ["int8", "bf16"], 32, 32, 0.5, (1,)),
+    "one_query": (1, 4, 128, [5, 1], ["bf16", "bf16"], 16, 16, 1.0, ()),
+    "eight_segments": (130, 2, 128, [1, 63, 64, 65, 0, 128, 3, 130], ["bf16", "int8"] * 4, 128, 64, 0.8, ()),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_attention_small_cases(case):
+    n_q, H, d, lens, dts, bq, bk, dens, empty = CASES[case]
+    q, segs, mask = _rand_case(sum(map(ord, case)), n_q, H, d, lens, dts, bq, bk, dens, empty)
+    _say("attention", case)
+    out, lse = run_attn(q, segs, mask, bq, bk)
+    O, LSE = oracle.attention(q, segs, mask, bq, bk)
+    e = assert_attn_close(out, lse, O, LSE, case)
+    _say(f"   max-abs {e[0]:.2e}, rel-RMS {e[1]:.2e}")
+    for r in empty:
+        rows = slice(r * bq, min(n_q, (r + 1) * bq))
+        assert np.all(out[rows] == 0)
+
+
+def test_attention_custom_softmax_scale():
+    q, segs, mask = _rand_case(5, 200, 2, 128, [100, 200], ["bf16", "bf16"], 128, 128)
+    out, lse = run_attn(q, segs, mask, 128, 128, softmax_scale=0.03)
+    O, LSE = oracle.attention(q, segs, mask, 128, 128, softmax_scale=0.03)
+    assert_attn_close(out, lse, O, LSE, "scale 0.03")
+
+
+def test_attention_all_segments_empty_gives_zero_and_minus_inf():
+    q = W.normal_bf16(1, 0, (40, 2, 64))
+    segs = [{"k": np.zeros((0, 2, 64), np.uint16), "v": np.zeros((0, 2, 64), np.uint16), "dtype": "bf16"}]
+    out, lse = run_attn(q, segs, np.zeros((3, 0), np.uint8), 16, 16)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_nan_in_skipped_tiles_never_reaches_the_output():
+    q, segs, mask = _rand_case(9, 512, 2, 128, [512], ["bf16"], 128, 128, 0.4)
+    mask[:, 1] = 0
+    mask[np.arange(4), np.arange(4)] = 1
+    mask[1, 1] = 0
+    out_clean, _ = run_attn(q, segs, mask, 128, 128)
+    poisoned = {"k": segs[0]["k"].copy(), "v": segs[0]["v"].copy(), "dtype": "bf16"}
+    poisoned["k"][128:256] = 0x7FC0
+    poisoned["v"][128:256] = 0x7FC0
+    out_p, lse_p = run_attn(q, [poisoned], mask, 128, 128)
+    assert np.array_equal(out_p, out_clean)
+    assert np.all(np.isfinite(lse_p))
+
+
+def test_attention_is_deterministic():
+    q, segs, mask = _rand_case(3, 700, 3, 128, [300, 700], ["int8", "bf16"], 128, 128, 0.9)
+    a = run_attn(q, segs, mask, 128, 128)
+    b = run_attn(q, segs, mask, 128, 128)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled rows
+
+def _sample_rows(n_q, rng, k=24):
+    rows = set(range(0, 3)) | set(range(n_q - 3, n_q))
+    last_tile = (n_q - 1) // 128 * 128
+    rows |= {last_tile, min(n_q - 1, last_tile + 1)}
+    rows |= set(rng.choice(n_q, size=k, replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["wan13b", "wan13b_int8", "large_dit", "bsa_sr"])
+def test_full_size_hot_path_sampled(name):
+    """The benchmark's step at full size: [qknorm_rope3d] -> [kv_quant_int8 of the
+    cache] -> attn_fwd on the GPU; the oracle runs the same chain on the CPU and
+    computes the sampled rows."""
+    import torch
+    import streaming_video_dit_amd as sdit
+    cfg = W.CONFIGS[name]
+    inp = W.make_inputs(cfg)
+    H, d, n_q = cfg.n_heads, cfg.head_dim, cfg.n_q
+    _say("full size", name, "n_q", n_q, "keys", sum(cfg.seg_lens))
+    # --- GPU chain
+    if cfg.rope:
+        geo = (cfg.T, cfg.Hl, cfg.Wl, cfg.t0, cfg.split)
+        gq, gk = _gpu_rope(geo, inp.q, inp.k, inp.gamma_q, inp.gamma_k)
+    else:
+        gq, gk = inp.q, inp.k
+    gpu_quant = {}
+    for i, is8 in enumerate(cfg.seg_int8[:-1]):
+        if is8:
+            ck, sk = _gpu_quant(inp.cache_k[i])
+            cv, sv = _gpu_quant(inp.cache_v[i])
+            gpu_quant[i] = (ck, sk, cv, sv)
+    out, lse = run_attn(gq, segments_for_oracle(inp, gk, gpu_quant), inp.mask, cfg.block, cfg.block)
+    # --- oracle chain
+    if cfg.rope:
+        dt, dh, dw = cfg.split
+        rq = oracle.qknorm_rope3d(inp.q, inp.gamma_q, cfg.T, cfg.Hl, cfg.Wl, cfg.t0, dt, dh, dw)
+        rk = oracle.qknorm_rope3d(inp.k, inp.gamma_k, cfg.T, cfg.Hl, cfg.Wl, cfg.t0, dt, dh, dw)
+    else:
+        rq, rk = inp.q, inp.k
+    ref_quant = {}
+    for i, is8 in enumerate(cfg.seg_int8[:-1]):
+        if is8:
+            ck, sk = oracle.kv_quant_int8(inp.cache_k[i])
+            cv, sv = oracle.kv_quant_int8(inp.cache_v[i])
+            ref_quant[i] = (ck, sk, cv, sv)
+            assert np.array_equal(ck, gpu_quant[i][0]) and np.array_equal(cv, gpu_quant[i][2])
+    rows = _sample_rows(n_q, np.random.default_rng(cfg.seed))
+    O, LSE = oracle.attention(rq, segments_for_oracle(inp, rk, ref_quant), inp.mask, cfg.block, cfg.block,
+                              rows=rows)
+    e = assert_attn_close(out[rows], lse[:, rows], O, LSE, name)
+    _say(f"   {len(rows)} rows x {H} heads: max-abs {e[0]:.2e}, rel-RMS {e[1]:.2e}")
+    # every row, every head: finite output, and LSE finite where a key is visible
+    assert np.all((out & 0x7F80) != 0x7F80)
