@@ -90,7 +90,7 @@ const char* sdit_last_error(void);
  *   p_a * theta^(-2j/d_a),
  * p_a being the token's position on that axis. Tokens are in (t, h, w)
  * row-major order, w fastest: n -> t = t0 + n/(Hl*Wl), h = (n/Wl) % Hl,
- * w = n % Wl. Arithmetic is fp32 with one rounding to bf16 at the end.
+ * w = n % Wl. Arithmetic is fp64 with one rounding to bf16 at the end.
  *
  *   q_in, k_in     bf16 [T*Hl*Wl][n_heads][head_dim]
  *   q_out, k_out   bf16, same shape; may equal q_in / k_in (in place),
@@ -144,6 +144,9 @@ int sdit_kv_quant_int8(const void* x, int8_t* codes, float* scales,
  * For query i with visible keys V(i) = {j : mask[qb(i)][kb(j)] != 0}:
  *   s_j = scale * q_i . k_j,  o_i = sum_j softmax(s)_j v_j,  lse_i = log sum_j e^{s_j};
  * a query with no visible key gets o_i = 0 and lse_i = -inf.
+ * Scores accumulate in fp32 from bf16 q.k products; the probability-weighted
+ * sum of V runs in fp16 with fp32 accumulation, so bf16 V values must stay
+ * below 65504 in magnitude (int8 codes always fit).
  * Output must not overlap any input. */
 int sdit_attn_fwd(const void* q, int32_t n_q,
                   const sdit_kv_segment* segs, int32_t n_segs,

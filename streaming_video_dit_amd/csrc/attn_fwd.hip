@@ -21,10 +21,14 @@
 //    every lane then owns ONE query column and 16 keys, so row max/sum are
 //    per-lane plus one v_permlane32_swap, and the rescale of O is a per-lane
 //    scalar.
-//  * O^T += V^T P^T: the S^T accumulator, converted to bf16, is directly the
-//    B operand; V is written to LDS transposed ([d][key]) with the middle two
-//    quads of every 16 keys swapped, which is exactly the key order in which
-//    the accumulator hands P over, so one 16-byte LDS read feeds each MFMA.
+//  * O^T += V^T P^T with v_mfma_f32_32x32x16_f16: the S^T accumulator,
+//    converted to fp16, is directly the B operand; V is written to LDS as fp16,
+//    transposed ([d][key]) with the middle two quads of every 16 keys swapped,
+//    which is exactly the key order in which the accumulator hands P over, so
+//    one 16-byte LDS read feeds each MFMA. P and V are fp16 rather than bf16
+//    at the same MFMA rate: fp16 has 3 more mantissa bits, and the rounding of
+//    P is the dominant error of the output when one key carries most of the
+//    weight. bf16 V converts exactly for |v| < 65504; int8 codes always do.
 //  * Online softmax in base 2 (scale*log2(e) folded in), with a lazy running
 //    max: O and l are only rescaled when a row max grows by more than 2^8, so
 //    P stays <= 256 and the rescale is skipped for almost every tile.
@@ -32,9 +36,10 @@
 //    LDS list (chunks of 512 candidates); skipped tiles cost nothing and are
 //    never read. Tiles whose mask blocks are only partly kept (block sizes
 //    below the tile) and ragged segment tails take a per-element path.
-//  * int8 segments: codes are widened exactly to bf16 while staging into LDS;
-//    the per-key K scale multiplies score rows and the per-key V scale
-//    multiplies P before its bf16 rounding (no lossy dequantised copy).
+//  * int8 segments: codes are widened exactly (K to bf16, V to fp16) while
+//    staging into LDS; the per-key K scale multiplies score rows and the
+//    per-key V scale multiplies P before its fp16 rounding (no lossy
+//    dequantised copy).
 //  * Grid is remapped so consecutive (head, q-tile) work items land on the
 //    same XCD and share its L2 for K/V.
 #include "sdit_internal.h"
@@ -43,6 +48,8 @@ namespace sdit {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BQ = kAttnBQ;
@@ -58,7 +65,7 @@ struct Smem {
   static constexpr int KS = D + 8;    // K row stride in LDS (bf16 elements)
   static constexpr int VS = BK + 8;   // V^T row stride in LDS (bf16 elements)
   uint16_t k[2][BK * KS];
-  uint16_t vt[2][D * VS];
+  uint16_t vt[2][D * VS];             // fp16
   float ksc[2][BK];                   // int8 tiles: k_scale * scale_log2
   float vsc[2][BK];                   // int8 tiles: v_scale
   uint16_t list[LIST_CAP];
@@ -203,22 +210,22 @@ __device__ __forceinline__ void store_tile(const AttnParams& p, const TileInfo& 
     const int pos = vt_pos(kq * 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      uint32_t v4[4];
+      float f[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t val;
         if (!i8) {
           const uint32_t w = (e >> 1) == 0 ? st.v[j].x : (e >> 1) == 1 ? st.v[j].y : (e >> 1) == 2 ? st.v[j].z : st.v[j].w;
-          val = (e & 1) ? (w >> 16) : (w & 0xFFFF);
+          f[j] = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
         } else {
           const uint32_t w = (e < 4) ? st.v[j].x : st.v[j].y;
-          const int c = (int)(int8_t)((w >> (8 * (e & 3))) & 0xFF);
-          val = __float_as_uint((float)c) >> 16;
+          f[j] = (float)(int)(int8_t)((w >> (8 * (e & 3))) & 0xFF);
         }
-        v4[j] = val;
       }
+      f16x2 lo, hi;
+      lo[0] = (_Float16)f[0]; lo[1] = (_Float16)f[1];
+      hi[0] = (_Float16)f[2]; hi[1] = (_Float16)f[3];
       *reinterpret_cast<uint2*>(vl + (dg * 8 + e) * VS + pos) =
-          make_uint2(v4[0] | (v4[1] << 16), v4[2] | (v4[3] << 16));
+          make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
     }
   }
 }
@@ -427,7 +434,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
       }
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
-      bf16x8 pb[4];
+      f16x8 pb[4];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         float pv[16];
@@ -448,9 +455,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          bf16x8 v;
+          f16x8 v;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = (__bf16)pv[8 * half + j];
+          for (int j = 0; j < 8; ++j) v[j] = (_Float16)pv[8 * half + j];
           pb[2 * kt + half] = v;
         }
       }
@@ -460,8 +467,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vl + (dt * 32 + r) * VS + kk * 16 + 8 * hh);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], o[dt], 0, 0, 0);
+          const f16x8 a = *reinterpret_cast<const f16x8*>(vl + (dt * 32 + r) * VS + kk * 16 + 8 * hh);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[kk], o[dt], 0, 0, 0);
         }
 
       if (has_next) store_tile<D>(p, tn, st, sm, buf ^ 1);

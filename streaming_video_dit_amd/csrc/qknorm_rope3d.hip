@@ -11,10 +11,12 @@
 // tensor (q or k) and a group of up to kHeadsPerUnit heads, handled by d/8
 // lanes that each own 8 consecutive columns (16 B per row, coalesced 256 B
 // rows). A lane's four rotation angles depend only on the token, so they are
-// computed once per unit and reused for every head of the unit. Angles are
-// formed and reduced modulo 2*pi in fp64 and only then handed to sincosf, so
-// the rotation error stays near one binary32 rounding even for the largest
-// positions (w up to ~100 at theta^0).
+// computed once per unit and reused for every head of the unit.
+// The arithmetic is fp64 (full rate on CDNA4 vector units, so it costs the
+// same as fp32 here), ending in one correctly rounded fp64 -> bf16
+// conversion. In fp32 a rotation whose two products nearly cancel loses
+// several bf16 ulps of its small result; in fp64 every output is within one
+// ulp of the exact value.
 #include "sdit_internal.h"
 
 namespace sdit {
@@ -26,10 +28,19 @@ constexpr int kHeadsPerUnit = 4;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo;
-  const __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+// fp64 -> bf16, round to nearest even, in one step. The fp32 rounding is
+// exact unless the fp32 result sits exactly half-way between two bf16 values
+// while the fp64 value does not; then the tie is broken by the side the fp64
+// value lies on (finite inputs only).
+__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+  const float f = (float)x;
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0xFFFFu) == 0x8000u && (double)f != x) {
+    const bool away = fabs(x) > fabs((double)f);
+    u = away ? u + 1u : u - 1u;
+  }
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
 }
 
 template <int D>
@@ -72,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
   const int pos_h = (tok / p.Wl) % p.Hl;
   const int pos_w = tok % p.Wl;
 
-  float cs[4], sn[4];
+  double cs[4], sn[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = c0 + 2 * i;           // first column of the pair
@@ -85,36 +96,33 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
       pos = pos_w; j = (c - p.d_t - p.d_h) / 2; da = p.d_w;
     }
     const double omega = exp2(-2.0 * (double)j / (double)da * p.log2_theta);
-    double phi = (double)pos * omega;
-    const double two_pi = 6.283185307179586476925286766559;
-    phi -= two_pi * rint(phi / two_pi);  // |phi| <= pi
-    sincosf((float)phi, &sn[i], &cs[i]);
+    sincos((double)pos * omega, &sn[i], &cs[i]);
   }
 
 #pragma unroll
   for (int i = 0; i < kHeadsPerUnit; ++i) {
-    float x[8];
+    double x[8];
     const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[2 * e] = bf16_lo(w[e]);
-      x[2 * e + 1] = bf16_hi(w[e]);
+      x[2 * e] = (double)bf16_lo(w[e]);
+      x[2 * e + 1] = (double)bf16_hi(w[e]);
     }
-    float ss = 0.f;
+    double ss = 0.0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+    for (int e = 0; e < 8; ++e) ss = fma(x[e], x[e], ss);
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-    const float inv = 1.0f / sqrtf(ss / (float)D + p.eps);
+    const double inv = 1.0 / sqrt(ss / (double)D + (double)p.eps);
 
     uint32_t o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float y0 = x[2 * e] * inv * g[2 * e];
-      const float y1 = x[2 * e + 1] * inv * g[2 * e + 1];
-      const float r0 = y0 * cs[e] - y1 * sn[e];
-      const float r1 = y0 * sn[e] + y1 * cs[e];
-      o[e] = pack_bf16x2(r0, r1);
+      const double y0 = x[2 * e] * inv * (double)g[2 * e];
+      const double y1 = x[2 * e + 1] * inv * (double)g[2 * e + 1];
+      const double r0 = y0 * cs[e] - y1 * sn[e];
+      const double r1 = y0 * sn[e] + y1 * cs[e];
+      o[e] = f64_to_bf16(r0) | (f64_to_bf16(r1) << 16);
     }
     if (active && i < nh)
       *reinterpret_cast<uint4*>(out + ((int64_t)tok * p.n_heads + h0 + i) * D + c0) =

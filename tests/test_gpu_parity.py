@@ -150,7 +150,7 @@ def test_tiny_workload_end_to_end(name):
     out, lse = run_attn(gq, segments_for_oracle(inp, gk), inp.mask, cfg.block, cfg.block)
     O, LSE = oracle.attention(rq, segments_for_oracle(inp, rk), inp.mask, cfg.block, cfg.block)
     e = assert_attn_close(out, lse, O, LSE, name)
-    _say(f"   max-abs {e[0]:.2e}, rel-RMS {e[1]:.2e}")
+    _say(f"   max-abs {e[0]:.2e} ({e[2]:.2e} beyond half an ulp), rel-RMS {e[1]:.2e}")
 
 
 def test_tiny_mask_readings_differ_on_gpu():
@@ -207,7 +207,7 @@ def test_attention_small_cases(case):
     out, lse = run_attn(q, segs, mask, bq, bk)
     O, LSE = oracle.attention(q, segs, mask, bq, bk)
     e = assert_attn_close(out, lse, O, LSE, case)
-    _say(f"   max-abs {e[0]:.2e}, rel-RMS {e[1]:.2e}")
+    _say(f"   max-abs {e[0]:.2e} ({e[2]:.2e} beyond half an ulp), rel-RMS {e[1]:.2e}")
     for r in empty:
         rows = slice(r * bq, min(n_q, (r + 1) * bq))
         assert np.all(out[rows] == 0)
@@ -232,13 +232,18 @@ def test_nan_in_skipped_tiles_never_reaches_the_output():
     mask[:, 1] = 0
     mask[np.arange(4), np.arange(4)] = 1
     mask[1, 1] = 0
-    out_clean, _ = run_attn(q, segs, mask, 128, 128)
+    out_clean, lse_clean = run_attn(q, segs, mask, 128, 128)
     poisoned = {"k": segs[0]["k"].copy(), "v": segs[0]["v"].copy(), "dtype": "bf16"}
     poisoned["k"][128:256] = 0x7FC0
     poisoned["v"][128:256] = 0x7FC0
     out_p, lse_p = run_attn(q, [poisoned], mask, 128, 128)
     assert np.array_equal(out_p, out_clean)
-    assert np.all(np.isfinite(lse_p))
+    assert np.array_equal(lse_p.view(np.uint32), lse_clean.view(np.uint32))
+    assert not np.isnan(lse_p).any()
+    # q-block 1 keeps no tile at all: zero output, LSE -inf
+    assert np.all(out_p[128:256] == 0) and np.all(np.isneginf(lse_p[:, 128:256]))
+    O, LSE = oracle.attention(q, segs, mask, 128, 128)
+    assert_attn_close(out_p, lse_p, O, LSE, "poisoned")
 
 
 def test_attention_is_deterministic():
@@ -300,6 +305,6 @@ def test_full_size_hot_path_sampled(name):
     O, LSE = oracle.attention(rq, segments_for_oracle(inp, rk, ref_quant), inp.mask, cfg.block, cfg.block,
                               rows=rows)
     e = assert_attn_close(out[rows], lse[:, rows], O, LSE, name)
-    _say(f"   {len(rows)} rows x {H} heads: max-abs {e[0]:.2e}, rel-RMS {e[1]:.2e}")
+    _say(f"   {len(rows)} rows x {H} heads: max-abs {e[0]:.2e} ({e[2]:.2e} beyond half an ulp), rel-RMS {e[1]:.2e}")
     # every row, every head: finite output, and LSE finite where a key is visible
     assert np.all((out & 0x7F80) != 0x7F80)
