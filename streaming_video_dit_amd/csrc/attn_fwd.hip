@@ -80,7 +80,6 @@ constexpr int LIST_CAP = 512;
 constexpr float TAU = 8.0f;           // lazy-rescale threshold (log2 units)
 constexpr float MASK_BIAS = -1.0e30f; // added to scores of keys that must not count
 constexpr int NXCD = 8;
-constexpr int PF = 4;                 // LDS operand reads in flight ahead of the MFMA
 
 template <int D>
 struct Layout {
@@ -158,39 +157,66 @@ struct Stage {
   float ks, vs;
 };
 
+// Per-thread load geometry, fixed for the whole kernel: element offsets (from
+// a tile's first row, head included) of every chunk this thread moves.
+template <int D>
+struct LoadPlan {
+  static constexpr int KMAX = (Layout<D>::K_BLKS + NW - 1) / NW;   // direct-load blocks per wave
+  int k_off[KMAX];   // bf16 K, padded-tile block wave + NW*i (padding chunks reload chunk 0)
+  int v_off;         // bf16 V chunk j adds j * (NT / CPR) rows
+  int i8_off;        // int8 K/V chunk j adds j * (NT / (D/16)) rows
+};
+
+template <int D>
+__device__ __forceinline__ void make_plan(LoadPlan<D>& pl, int row_stride) {
+  using L = Layout<D>;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int i = 0; i < LoadPlan<D>::KMAX; ++i) {
+    const int lin = (wave + NW * i) * 64 + lane;
+    const int row = lin / L::K_CH, pc = lin % L::K_CH;
+    pl.k_off[i] = row * row_stride + (pc < L::CPR ? pc : 0) * 8;
+  }
+  pl.v_off = (tid / L::CPR) * row_stride + (tid % L::CPR) * 8;
+  pl.i8_off = (tid / (D / 16)) * row_stride + (tid % (D / 16)) * 16;
+}
+
 // Start loading tile t into buffer buf: bf16 K directly into LDS, the rest
-// into registers (finished by commit_tile).
+// into registers (finished by commit_tile). Rows past the segment end are
+// loaded from its last row: their scores get the -1e30 bias, so their
+// probabilities are exactly 0 and any finite data there is harmless.
 template <int D, bool SCALED>
 __device__ __forceinline__ void issue_tile(const AttnParams& p, const TileInfo& t, int head, Stage<D>& st,
-                                           Smem<D>& sm, int buf) {
+                                           Smem<D>& sm, int buf, const LoadPlan<D>& pl) {
   using L = Layout<D>;
   const AttnSegment& sg = p.seg[t.seg];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int64_t row_stride = (int64_t)p.n_heads * D;   // elements between consecutive tokens
+  const int row_stride = p.n_heads * D;   // elements between consecutive tokens
   const int64_t base = ((int64_t)t.key0 * p.n_heads + head) * D;
-  if (!sg.is_int8) {
+  const bool ragged = t.n_valid < BK;
+  if (!SCALED || !sg.is_int8) {
     const uint16_t* kb = (const uint16_t*)sg.k + base;
     const uint16_t* vb = (const uint16_t*)sg.v + base;
-    // K: block blk (64 lanes, 1 KB) fills padded-tile chunks [blk*64, blk*64 + 64);
-    // a padding chunk reloads chunk 0 of its row, rows past the segment end
-    // reload its last row (both never count).
-#pragma unroll 1
-    for (int blk = wave; blk < L::K_BLKS; blk += NW) {
-      const int lin = blk * 64 + lane;
-      const int row = lin / L::K_CH;
-      const int pc = lin % L::K_CH;
-      const int c = pc < L::CPR ? pc : 0;
-      const int srow = min(row, t.n_valid - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(kb + srow * row_stride + c * 8),
-                                       (lds_void*)(sm.k[buf] + blk * 64 * 8), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < LoadPlan<D>::KMAX; ++i) {
+      const int blk = wave + NW * i;
+      if (blk < L::K_BLKS) {
+        int off = pl.k_off[i];
+        if (ragged) {
+          const int lin = blk * 64 + lane;
+          const int row = lin / L::K_CH, pc = lin % L::K_CH;
+          off = min(row, t.n_valid - 1) * row_stride + (pc < L::CPR ? pc : 0) * 8;
+        }
+        __builtin_amdgcn_global_load_lds((const void*)(kb + off), (lds_void*)(sm.k[buf] + blk * 64 * 8), 16, 0, 0);
+      }
     }
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
-      const int lin = tid + j * NT;
-      const int row = lin / L::CPR, c = lin % L::CPR;
-      st.r[j] = (row < t.n_valid) ? *reinterpret_cast<const uint4*>(vb + row * row_stride + c * 8)
-                                  : make_uint4(0, 0, 0, 0);
+      constexpr int RSTEP = NT / L::CPR;
+      int off = pl.v_off + j * RSTEP * row_stride;
+      if (ragged) off = min(tid / L::CPR + j * RSTEP, t.n_valid - 1) * row_stride + (tid % L::CPR) * 8;
+      st.r[j] = *reinterpret_cast<const uint4*>(vb + off);
     }
     if (SCALED && tid < BK) {
       st.ks = p.scale_log2;
@@ -201,18 +227,19 @@ __device__ __forceinline__ void issue_tile(const AttnParams& p, const TileInfo& 
     const int8_t* vb = (const int8_t*)sg.v + base;
 #pragma unroll
     for (int j = 0; j < D / 64; ++j) {
-      const int lin = tid + j * NT;
-      const int row = lin / (D / 16), c = lin % (D / 16);
-      const bool ok = row < t.n_valid;
-      st.r[j] = ok ? *reinterpret_cast<const uint4*>(kb + row * row_stride + c * 16) : make_uint4(0, 0, 0, 0);
-      st.r[D / 64 + j] = ok ? *reinterpret_cast<const uint4*>(vb + row * row_stride + c * 16) : make_uint4(0, 0, 0, 0);
+      constexpr int RSTEP = NT / (D / 16);
+      int off = pl.i8_off + j * RSTEP * row_stride;
+      if (ragged) off = min(tid / (D / 16) + j * RSTEP, t.n_valid - 1) * row_stride + (tid % (D / 16)) * 16;
+      st.r[j] = *reinterpret_cast<const uint4*>(kb + off);
+      st.r[D / 64 + j] = *reinterpret_cast<const uint4*>(vb + off);
     }
     if (tid < BK) {
       // keys past the segment end keep a positive K multiplier so their bias stays -1e30
       const bool ok = tid < t.n_valid;
-      const int64_t si = (int64_t)(t.key0 + tid) * p.n_heads + head;
-      st.ks = ok ? sg.k_scale[si] * p.scale_log2 : p.scale_log2;
-      st.vs = ok ? sg.v_scale[si] : 0.f;
+      const int64_t si = (int64_t)(t.key0 + min(tid, t.n_valid - 1)) * p.n_heads + head;
+      const float ksv = sg.k_scale[si], vsv = sg.v_scale[si];
+      st.ks = ok ? ksv * p.scale_log2 : p.scale_log2;
+      st.vs = ok ? vsv : 0.f;
     }
   }
 }
@@ -222,7 +249,7 @@ __device__ __forceinline__ void commit_tile(const AttnParams& p, const TileInfo&
                                             Smem<D>& sm, int buf) {
   using L = Layout<D>;
   const int tid = threadIdx.x;
-  if (!p.seg[t.seg].is_int8) {
+  if (!SCALED || !p.seg[t.seg].is_int8) {
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
       const int lin = tid + j * NT;
@@ -296,6 +323,8 @@ __device__ __forceinline__ void compute_tile(const AttnParams& p, const TileInfo
   using L = Layout<D>;
   constexpr int NKS = D / 16;
   constexpr int NDT = D / 32;
+  // LDS operand reads in flight ahead of their MFMA (the scaled path needs the registers)
+  constexpr int PF = SCALED ? 2 : 4;
 
   // ---- S^T = K Q^T for two 32-key subtiles; operand reads PF steps ahead,
   // scheduling fences keep the compiler from hoisting all of them
@@ -505,6 +534,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
 
   int buf = 0;
   Stage<D> st;
+  LoadPlan<D> plan;
+  make_plan<D>(plan, p.n_heads * D);
 
 #pragma unroll 1
   for (int cbase = 0; cbase < p.n_tiles; cbase += LIST_CAP) {
@@ -549,20 +580,20 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
     // ---- prologue: first kept tile into LDS
     {
       const TileInfo t = tile_info(p, cbase + sm.list[0]);
-      issue_tile<D, SCALED>(p, t, head, st, sm, buf);
+      issue_tile<D, SCALED>(p, t, head, st, sm, buf, plan);
       commit_tile<D, SCALED>(p, t, st, sm, buf);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
+    TileInfo tn = tile_info(p, cbase + sm.list[0]);
 #pragma unroll 1
     for (int it = 0; it < total; ++it) {
-      const TileInfo t = tile_info(p, cbase + sm.list[it]);
-      TileInfo tn;
+      const TileInfo t = tn;
       const bool has_next = it + 1 < total;
       if (has_next) {
         tn = tile_info(p, cbase + sm.list[it + 1]);
-        issue_tile<D, SCALED>(p, tn, head, st, sm, buf ^ 1);
+        issue_tile<D, SCALED>(p, tn, head, st, sm, buf ^ 1, plan);
       }
       compute_tile<D, SCALED, GENERAL>(p, t, ws, sm.k[buf], sm.v[buf], sm.ksc[buf], sm.vsc[buf], k_lane, v_lane,
                                        r, hh, my_qb, qb_lo, n_qbt);
