@@ -51,7 +51,8 @@
 //    tile) get a -1e30 bias added by one extra MFMA k-step: A[key][slot] is
 //    0 or -1e30, B[slot][q] selects the query's slot (its q-block), so no
 //    per-element compare/select is needed. -1e30 is finite, so no 0 x inf.
-//  * int8 segments: the per-key K scale multiplies score rows and the per-key
+//  * int8 segments: the per-key K scale (floored at 2^-40, so that the bias
+//    of a masked key stays far below any real score) multiplies score rows and the per-key
 //    V scale multiplies P before its fp16 rounding (no lossy dequantised
 //    copy). Calls with an int8 segment use that scaled path for every tile
 //    (bf16 tiles get scale_log2 and 1); calls without one use the cheaper
@@ -79,6 +80,11 @@ constexpr int NT = NW * 64;
 constexpr int LIST_CAP = 512;
 constexpr float TAU = 8.0f;           // lazy-rescale threshold (log2 units)
 constexpr float MASK_BIAS = -1.0e30f; // added to scores of keys that must not count
+// A row max below this comes only from biased keys: such a tile holds nothing
+// visible for the row. Real scores in log2 units stay far above it, and a
+// biased key stays below it because every score multiplier is >= KSC_MIN.
+constexpr float MASKED_MAX = -1.0e15f;
+constexpr float KSC_MIN = 0x1p-40f;   // floor of the per-key score multiplier
 constexpr int NXCD = 8;
 
 template <int D>
@@ -238,7 +244,7 @@ __device__ __forceinline__ void issue_tile(const AttnParams& p, const TileInfo& 
       const bool ok = tid < t.n_valid;
       const int64_t si = (int64_t)(t.key0 + min(tid, t.n_valid - 1)) * p.n_heads + head;
       const float ksv = sg.k_scale[si], vsv = sg.v_scale[si];
-      st.ks = ok ? ksv * p.scale_log2 : p.scale_log2;
+      st.ks = ok ? fmaxf(ksv * p.scale_log2, KSC_MIN) : p.scale_log2;
       st.vs = ok ? vsv : 0.f;
     }
   }
@@ -403,6 +409,7 @@ __device__ __forceinline__ void compute_tile(const AttnParams& p, const TileInfo
   // unscaled path: raw scores, scale_log2 folded into the exponent's FMA
   const float cs = SCALED ? 1.0f : p.scale_log2;
   mt = swap_halves_max(mt) * cs;
+  if (mt < MASKED_MAX) mt = -INFINITY;   // nothing visible for this row in the tile
 
   // ---- online softmax (lazy running max)
   const bool need = mt > ws.m_run + TAU;

@@ -246,6 +246,35 @@ def test_nan_in_skipped_tiles_never_reaches_the_output():
     assert_attn_close(out_p, lse_p, O, LSE, "poisoned")
 
 
+def test_rows_whose_first_tiles_are_fully_masked():
+    # 32-row q-blocks inside one 128-row tile: q-block 0 skips the first three
+    # 64-key tiles that its neighbours keep, so its rows meet whole tiles of
+    # -1e30-biased scores before any visible key. Their output must be the
+    # attention over the later keys only (no overflow from the bias).
+    q, segs, mask = _rand_case(21, 128, 2, 128, [512], ["bf16"], 32, 64)
+    mask[0, :3] = 0
+    mask[2, 5:] = 0
+    out, lse = run_attn(q, segs, mask, 32, 64)
+    O, LSE = oracle.attention(q, segs, mask, 32, 64)
+    assert not np.isnan(lse).any()
+    assert_attn_close(out, lse, O, LSE, "first tiles masked")
+
+
+def test_all_zero_int8_key_in_a_masked_block_stays_masked():
+    # An all-zero key quantises to scale 0; the mask bias must still remove it
+    # when its block is dropped for a q-block (its score multiplier is floored
+    # above 0), and it must count (score 0) where its block is kept.
+    q, segs, mask = _rand_case(22, 96, 2, 128, [200, 64], ["int8", "bf16"], 32, 32)
+    s = segs[0]
+    s["k"][40:48] = 0
+    s["k_scale"][40:48] = 0.0
+    mask[:] = 1
+    mask[1, 1] = 0          # keys 32..63 (holding the zero keys) dropped for rows 32..63
+    out, lse = run_attn(q, segs, mask, 32, 32)
+    O, LSE = oracle.attention(q, segs, mask, 32, 32)
+    assert_attn_close(out, lse, O, LSE, "zero int8 key")
+
+
 def test_attention_is_deterministic():
     q, segs, mask = _rand_case(3, 700, 3, 128, [300, 700], ["int8", "bf16"], 128, 128, 0.9)
     a = run_attn(q, segs, mask, 128, 128)
