@@ -104,6 +104,22 @@ class Step:
             ev_after.record()
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs summarised under profiles/ (calibrated against a plain copy). The
+    figures belong to one version of the kernel source: once attn_fwd.hip has
+    changed they no longer describe it and None is returned."""
+    f = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
+    if not os.path.exists(f):
+        return None
+    t = json.load(open(f))
+    src = os.path.join(ROOT, "streaming_video_dit_amd", "csrc", "attn_fwd.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != t.get("attn_fwd_src_sha256_16"):
+        return None
+    w = t["workloads"].get(workload)
+    return None if w is None else int(w["fetch_bytes"] + w["write_bytes"])
+
+
 def cpu_baseline(cfg: W.Config, budget_s: float = 10.0):
     """The oracle as it stands, on the host: qknorm_rope3d of the chunk (and
     the int8 quantisation of the cache for the int8 workload) once, then
@@ -234,7 +250,8 @@ def main():
         "wall_s_timed": round(t_wall, 3),
         "roofline": {"kernel": "attn_fwd_kernel<128>" if cfg.head_dim == 128 else "attn_fwd_kernel<64>",
                      "bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(cfg.name)},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
