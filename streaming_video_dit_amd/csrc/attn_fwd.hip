@@ -10,15 +10,24 @@
 // Block-Sparse-Attention section).
 //
 // How (MI355X design):
-//  * One workgroup = one head x 128 query rows, 4 waves of 32 rows each; two
-//    workgroups per CU (LDS ~76 KB each) so two waves share every SIMD and
-//    one wave's softmax overlaps the other's matrix work.
-//  * Keys stream through LDS in 64-key tiles, double buffered, one barrier
-//    per tile. bf16 K goes straight from global memory into LDS
-//    (global_load_lds_dwordx4: lane t lands at base + 16 t, so each lane's
-//    source address is chosen to realise the padded layout below). V is
-//    staged through registers once per workgroup and converted to fp16; int8
-//    K/V codes are widened exactly on the same path.
+//  * One workgroup = one head x 256 query rows, 8 waves of 32 rows each, one
+//    workgroup per CU (LDS ~105 KB), so two waves share every SIMD. Waves
+//    4..7 run half a tile behind waves 0..3: in each step they first
+//    multiply the previous tile's P with V, then compute the current tile's
+//    scores and softmax, while waves 0..3 do scores, softmax, P.V of the
+//    current tile. On every SIMD one wave's softmax (vector ALU) then
+//    overlaps the other wave's matrix work. A 64-key K/V tile loaded once
+//    serves all 256 rows.
+//  * Keys stream through LDS in 64-key tiles, one barrier per tile. K is
+//    double buffered, V triple buffered (the lagging waves still read tile
+//    i-1 while tile i+1 is written). bf16 K goes straight from global memory
+//    into LDS (global_load_lds_dwordx4: lane t lands at base + 16 t, so each
+//    lane's source address is chosen to realise the padded layout below). V
+//    is staged through registers and converted to fp16; int8 K/V codes are
+//    widened exactly on the same path. Each wave's share of the next tile's
+//    loads is issued between its score MFMAs rather than all at once (a
+//    burst from every wave queues in the CU's address unit and stalls the
+//    issuing waves).
 //  * LDS tiles are row-major ([key][d]) with padded rows: K rows are D+8
 //    bf16 (16 rows read at one column land on 16 different 4-bank groups), V
 //    rows are D+32 fp16 (the 4 rows x 64 bytes that one transposed read
@@ -44,13 +53,19 @@
 //  * Online softmax in base 2 (scale*log2(e) folded in), with a lazy running
 //    max: O and l are only rescaled when a row max grows by more than 2^8, so
 //    P stays <= 256 and the rescale is skipped for almost every tile.
-//  * Mask: each workgroup compacts the kept 64-key tiles of its q-tile into an
-//    LDS list (chunks of 512 candidates); skipped tiles cost nothing and are
-//    never read. Keys that must not count inside a processed tile (past a
-//    segment end, or in a dropped block when mask blocks are smaller than the
-//    tile) get a -1e30 bias added by one extra MFMA k-step: A[key][slot] is
-//    0 or -1e30, B[slot][q] selects the query's slot (its q-block), so no
-//    per-element compare/select is needed. -1e30 is finite, so no 0 x inf.
+//  * Mask: each workgroup compacts the kept 64-key tiles of its 256 rows into
+//    an LDS list of packed descriptors (key offset, segment, valid keys, and
+//    which waves have a kept (q-block, k-block) pair in the tile), passes of
+//    1024 candidates; skipped tiles cost nothing and are never read, a wave
+//    whose rows keep nothing in a listed tile skips its compute, and the
+//    loop reads one descriptor per tile instead of searching the segment
+//    table. Keys that must not count inside a processed tile (past a segment
+//    end, or in a dropped block when mask blocks are finer than a wave's 32
+//    rows or the 64-key tile) get a -1e30 bias added by one extra MFMA
+//    k-step: A[key][slot] is 0 or -1e30, B[slot][q] selects the query's slot
+//    (its q-block inside the workgroup, up to 16 slots over the two lane
+//    halves), so no per-element compare/select is needed. -1e30 is finite,
+//    so no 0 x inf.
 //  * int8 segments: the per-key K scale (floored at 2^-40, so that the bias
 //    of a masked key stays far below any real score) multiplies score rows and the per-key
 //    V scale multiplies P before its fp16 rounding (no lossy dequantised
@@ -75,9 +90,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BQ = kAttnBQ;
 constexpr int BK = kAttnBK;
-constexpr int NW = 4;
+constexpr int NW = 8;                 // waves per workgroup, 32 query rows each
 constexpr int NT = NW * 64;
-constexpr int LIST_CAP = 512;
+constexpr int LIST_CAP = 2 * NT;      // kept-tile list entries per compaction pass
+constexpr int NVBUF = 3;              // V tiles in flight: two being read, one being written
 constexpr float TAU = 8.0f;           // lazy-rescale threshold (log2 units)
 constexpr float MASK_BIAS = -1.0e30f; // added to scores of keys that must not count
 // A row max below this comes only from biased keys: such a tile holds nothing
@@ -86,6 +102,7 @@ constexpr float MASK_BIAS = -1.0e30f; // added to scores of keys that must not c
 constexpr float MASKED_MAX = -1.0e15f;
 constexpr float KSC_MIN = 0x1p-40f;   // floor of the per-key score multiplier
 constexpr int NXCD = 8;
+static_assert(BQ == NW * 32, "one wave per 32 query rows");
 
 template <int D>
 struct Layout {
@@ -94,16 +111,22 @@ struct Layout {
   static constexpr int VS = D + 32;            // V row stride (fp16 elements)
   static constexpr int K_CH = KS / 8;          // chunks per padded K row
   static constexpr int K_BLKS = BK * K_CH / 64;  // 64-lane direct-load blocks per K tile
+  static constexpr int VCH = BK * CPR / NT;    // bf16 V chunks staged per thread
+  static constexpr int I8_THREADS = BK * (D / 16);  // threads moving 16 int8 codes of K and of V
+  static constexpr int I8CH = I8_THREADS >= NT ? I8_THREADS / NT : 1;
+  static constexpr int SR = VCH > 2 * I8CH ? VCH : 2 * I8CH;
   static_assert(BK * K_CH % 64 == 0, "K tile must be whole 64-lane blocks");
+  static_assert(VCH >= 1 && BK * CPR % NT == 0, "V tile must be whole chunks per thread");
+  static_assert(I8_THREADS % NT == 0 || I8_THREADS < NT, "int8 tile split");
 };
 
 template <int D>
 struct Smem {
-  uint16_t k[2][BK * Layout<D>::KS];  // bf16, padded rows
-  uint16_t v[2][BK * Layout<D>::VS];  // fp16, padded rows
-  float ksc[2][BK];                   // scaled path: per-key multiplier of the raw score
-  float vsc[2][BK];                   // scaled path: per-key multiplier of P
-  uint16_t list[LIST_CAP];
+  uint16_t k[2][BK * Layout<D>::KS];      // bf16, padded rows
+  uint16_t v[NVBUF][BK * Layout<D>::VS];  // fp16, padded rows
+  float ksc[2][BK];                       // scaled path: per-key multiplier of the raw score
+  float vsc[2][BK];                       // scaled path: per-key multiplier of P
+  uint2 desc[LIST_CAP];                   // kept tiles of the current pass (pack_desc)
   int32_t wave_count[NW];
 };
 
@@ -122,6 +145,45 @@ __device__ __forceinline__ TileInfo tile_info(const AttnParams& p, int g) {
   t.seg = s;
   t.key0 = (g - p.seg[s].tile_start) * BK;
   t.n_valid = min(BK, p.seg[s].len - t.key0);
+  return t;
+}
+
+// A kept tile as the main loop sees it: wave-uniform values read once per
+// step from the LDS descriptor list and the segment table.
+struct TileRef {
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  int key0;
+  int n_valid;
+  int is_int8;
+  int kb_start;
+  int wmask;   // waves with a kept (q-block, k-block) pair in the tile
+};
+
+// descriptor: x = first key inside the segment, y = segment | n_valid << 8 | wave mask << 16
+__device__ __forceinline__ uint2 pack_desc(const TileInfo& t, uint32_t wmask) {
+  return make_uint2((uint32_t)t.key0, (uint32_t)t.seg | ((uint32_t)t.n_valid << 8) | (wmask << 16));
+}
+
+__device__ __forceinline__ TileRef tile_ref(const AttnParams& p, uint2 d) {
+  const uint32_t x = __builtin_amdgcn_readfirstlane(d.x);
+  const uint32_t y = __builtin_amdgcn_readfirstlane(d.y);
+  const AttnSegment& sg = p.seg[y & 0xFF];
+  TileRef t;
+  t.k = sg.k;
+  t.v = sg.v;
+  t.k_scale = sg.k_scale;
+  t.v_scale = sg.v_scale;
+  t.is_int8 = sg.is_int8;
+  t.kb_start = sg.kb_start;
+  t.key0 = (int)x;
+  t.n_valid = (int)((y >> 8) & 0xFF);
+  t.wmask = (int)(y >> 16);
+  // complete the scalar loads here, before the step's LDS traffic starts
+  // (their wait would otherwise also wait for every LDS read in flight)
+  asm volatile("" ::"s"(t.k), "s"(t.v), "s"(t.k_scale), "s"(t.v_scale), "s"(t.is_int8), "s"(t.kb_start));
   return t;
 }
 
@@ -155,11 +217,11 @@ __device__ __forceinline__ uint4 i8x8_to_f16x8(uint32_t w0, uint32_t w1) {
 }
 
 // Registers holding the register-staged part of one tile between its global
-// load and its LDS store. bf16 tiles: D/32 chunks of 8 V values. int8 tiles:
-// D/64 chunks of 16 K codes, then D/64 chunks of 16 V codes.
+// load and its LDS store. bf16 tiles: VCH chunks of 8 V values. int8 tiles:
+// I8CH chunks of 16 K codes, then I8CH chunks of 16 V codes.
 template <int D>
 struct Stage {
-  uint4 r[D / 32];
+  uint4 r[Layout<D>::SR];
   float ks, vs;
 };
 
@@ -187,63 +249,75 @@ __device__ __forceinline__ void make_plan(LoadPlan<D>& pl, int row_stride) {
   pl.i8_off = (tid / (D / 16)) * row_stride + (tid % (D / 16)) * 16;
 }
 
-// Start loading tile t into buffer buf: bf16 K directly into LDS, the rest
-// into registers (finished by commit_tile). Rows past the segment end are
-// loaded from its last row: their scores get the -1e30 bias, so their
+// Loads of one tile, cut into NPART pieces of one or two wave instructions
+// each so that they can be spread over a wave's matrix work (every wave
+// issuing a whole tile at once queues its instructions behind the other
+// waves' in the CU's address unit). bf16 tiles: K goes directly into LDS
+// buffer kbuf, V into registers (finished by commit_tile). int8 tiles: K and
+// V codes into registers, then the per-key scales. Rows past the segment end
+// are loaded from its last row: their scores get the -1e30 bias, so their
 // probabilities are exactly 0 and any finite data there is harmless.
+template <int D>
+struct TileLoad {
+  static constexpr int KMAX = LoadPlan<D>::KMAX;
+  static constexpr int NB16 = KMAX + Layout<D>::VCH;
+  static constexpr int NI8 = 2 * Layout<D>::I8CH + 1;
+  static constexpr int NPART = NB16 > NI8 ? NB16 : NI8;
+};
+
 template <int D, bool SCALED>
-__device__ __forceinline__ void issue_tile(const AttnParams& p, const TileInfo& t, int head, Stage<D>& st,
-                                           Smem<D>& sm, int buf, const LoadPlan<D>& pl) {
+__device__ __forceinline__ void issue_part(const AttnParams& p, const TileRef& t, int head, Stage<D>& st,
+                                           Smem<D>& sm, int kbuf, const LoadPlan<D>& pl, int j) {
   using L = Layout<D>;
-  const AttnSegment& sg = p.seg[t.seg];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int row_stride = p.n_heads * D;   // elements between consecutive tokens
   const int64_t base = ((int64_t)t.key0 * p.n_heads + head) * D;
   const bool ragged = t.n_valid < BK;
-  if (!SCALED || !sg.is_int8) {
-    const uint16_t* kb = (const uint16_t*)sg.k + base;
-    const uint16_t* vb = (const uint16_t*)sg.v + base;
-#pragma unroll
-    for (int i = 0; i < LoadPlan<D>::KMAX; ++i) {
-      const int blk = wave + NW * i;
+  if (!SCALED || !t.is_int8) {
+    const uint16_t* kb = (const uint16_t*)t.k + base;
+    const uint16_t* vb = (const uint16_t*)t.v + base;
+    if (j < TileLoad<D>::KMAX) {
+      const int blk = wave + NW * j;
       if (blk < L::K_BLKS) {
-        int off = pl.k_off[i];
+        int off = pl.k_off[j];
         if (ragged) {
           const int lin = blk * 64 + lane;
           const int row = lin / L::K_CH, pc = lin % L::K_CH;
           off = min(row, t.n_valid - 1) * row_stride + (pc < L::CPR ? pc : 0) * 8;
         }
-        __builtin_amdgcn_global_load_lds((const void*)(kb + off), (lds_void*)(sm.k[buf] + blk * 64 * 8), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(kb + off), (lds_void*)(sm.k[kbuf] + blk * 64 * 8), 16, 0, 0);
       }
-    }
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j) {
+    } else if (j < TileLoad<D>::NB16) {
+      const int jv = j - TileLoad<D>::KMAX;
       constexpr int RSTEP = NT / L::CPR;
-      int off = pl.v_off + j * RSTEP * row_stride;
-      if (ragged) off = min(tid / L::CPR + j * RSTEP, t.n_valid - 1) * row_stride + (tid % L::CPR) * 8;
-      st.r[j] = *reinterpret_cast<const uint4*>(vb + off);
+      int off = pl.v_off + jv * RSTEP * row_stride;
+      if (ragged) off = min(tid / L::CPR + jv * RSTEP, t.n_valid - 1) * row_stride + (tid % L::CPR) * 8;
+      st.r[jv] = *reinterpret_cast<const uint4*>(vb + off);
     }
-    if (SCALED && tid < BK) {
+    if (SCALED && j == 0 && tid < BK) {
       st.ks = p.scale_log2;
       st.vs = tid < t.n_valid ? 1.0f : 0.0f;
     }
   } else {
-    const int8_t* kb = (const int8_t*)sg.k + base;
-    const int8_t* vb = (const int8_t*)sg.v + base;
-#pragma unroll
-    for (int j = 0; j < D / 64; ++j) {
-      constexpr int RSTEP = NT / (D / 16);
-      int off = pl.i8_off + j * RSTEP * row_stride;
-      if (ragged) off = min(tid / (D / 16) + j * RSTEP, t.n_valid - 1) * row_stride + (tid % (D / 16)) * 16;
-      st.r[j] = *reinterpret_cast<const uint4*>(kb + off);
-      st.r[D / 64 + j] = *reinterpret_cast<const uint4*>(vb + off);
-    }
-    if (tid < BK) {
+    const int8_t* kb = (const int8_t*)t.k + base;
+    const int8_t* vb = (const int8_t*)t.v + base;
+    if (j < 2 * L::I8CH) {
+      if (L::I8_THREADS >= NT || tid < L::I8_THREADS) {
+        const int ji = j % L::I8CH;
+        constexpr int RSTEP = NT / (D / 16);
+        int off = pl.i8_off + ji * RSTEP * row_stride;
+        if (ragged) off = min(tid / (D / 16) + ji * RSTEP, t.n_valid - 1) * row_stride + (tid % (D / 16)) * 16;
+        if (j < L::I8CH)
+          st.r[ji] = *reinterpret_cast<const uint4*>(kb + off);
+        else
+          st.r[L::I8CH + ji] = *reinterpret_cast<const uint4*>(vb + off);
+      }
+    } else if (j == 2 * L::I8CH && tid < BK) {
       // keys past the segment end keep a positive K multiplier so their bias stays -1e30
       const bool ok = tid < t.n_valid;
       const int64_t si = (int64_t)(t.key0 + min(tid, t.n_valid - 1)) * p.n_heads + head;
-      const float ksv = sg.k_scale[si], vsv = sg.v_scale[si];
+      const float ksv = t.k_scale[si], vsv = t.v_scale[si];
       st.ks = ok ? fmaxf(ksv * p.scale_log2, KSC_MIN) : p.scale_log2;
       st.vs = ok ? vsv : 0.f;
     }
@@ -251,25 +325,34 @@ __device__ __forceinline__ void issue_tile(const AttnParams& p, const TileInfo& 
 }
 
 template <int D, bool SCALED>
-__device__ __forceinline__ void commit_tile(const AttnParams& p, const TileInfo& t, const Stage<D>& st,
-                                            Smem<D>& sm, int buf) {
+__device__ __forceinline__ void issue_tile(const AttnParams& p, const TileRef& t, int head, Stage<D>& st,
+                                           Smem<D>& sm, int kbuf, const LoadPlan<D>& pl) {
+#pragma unroll
+  for (int j = 0; j < TileLoad<D>::NPART; ++j) issue_part<D, SCALED>(p, t, head, st, sm, kbuf, pl, j);
+}
+
+// Finish tile t: register-staged V (and int8 K) into LDS buffers vbuf (kbuf),
+// scaled-path multipliers into slot kbuf.
+template <int D, bool SCALED>
+__device__ __forceinline__ void commit_tile(const TileRef& t, const Stage<D>& st, Smem<D>& sm, int kbuf,
+                                            int vbuf) {
   using L = Layout<D>;
   const int tid = threadIdx.x;
-  if (!SCALED || !p.seg[t.seg].is_int8) {
+  if (!SCALED || !t.is_int8) {
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j) {
+    for (int j = 0; j < L::VCH; ++j) {
       const int lin = tid + j * NT;
       const int row = lin / L::CPR, c = lin % L::CPR;
-      *reinterpret_cast<uint4*>(sm.v[buf] + row * L::VS + c * 8) = bf16x8_to_f16x8(st.r[j]);
+      *reinterpret_cast<uint4*>(sm.v[vbuf] + row * L::VS + c * 8) = bf16x8_to_f16x8(st.r[j]);
     }
-  } else {
+  } else if (L::I8_THREADS >= NT || tid < L::I8_THREADS) {
 #pragma unroll
-    for (int j = 0; j < D / 64; ++j) {
+    for (int j = 0; j < L::I8CH; ++j) {
       const int lin = tid + j * NT;
       const int row = lin / (D / 16), c16 = lin % (D / 16);
-      uint16_t* kr = sm.k[buf] + row * L::KS + 16 * c16;
-      uint16_t* vr = sm.v[buf] + row * L::VS + 16 * c16;
-      const uint4 kc = st.r[j], vc = st.r[D / 64 + j];
+      uint16_t* kr = sm.k[kbuf] + row * L::KS + 16 * c16;
+      uint16_t* vr = sm.v[vbuf] + row * L::VS + 16 * c16;
+      const uint4 kc = st.r[j], vc = st.r[L::I8CH + j];
       *reinterpret_cast<uint4*>(kr) = i8x8_to_bf16x8(kc.x, kc.y);
       *reinterpret_cast<uint4*>(kr + 8) = i8x8_to_bf16x8(kc.z, kc.w);
       *reinterpret_cast<uint4*>(vr) = i8x8_to_f16x8(vc.x, vc.y);
@@ -277,8 +360,8 @@ __device__ __forceinline__ void commit_tile(const AttnParams& p, const TileInfo&
     }
   }
   if (SCALED && tid < BK) {
-    sm.ksc[buf][tid] = st.ks;
-    sm.vsc[buf][tid] = st.vs;
+    sm.ksc[kbuf][tid] = st.ks;
+    sm.vsc[kbuf][tid] = st.vs;
   }
 }
 
@@ -318,14 +401,15 @@ struct WaveState {
   bool seen;           // general masks: a kept key reached this row
 };
 
-// One 64-key tile for one wave: S^T = K Q^T, masking bias, online softmax,
-// O^T += V^T P^T. Element e2 of score subtile kt is key kt*32 + 8*(e2/4) +
-// 4*hh + e2%4 of the tile.
-template <int D, bool SCALED, bool GENERAL>
-__device__ __forceinline__ void compute_tile(const AttnParams& p, const TileInfo& t, WaveState<D>& ws,
-                                             const uint16_t* kl, const uint16_t* vl, const float* ksc,
-                                             const float* vsc, int k_lane, int v_lane, int r, int hh,
-                                             int my_qb, int qb_lo, int n_qbt) {
+// First half of a 64-key tile for one wave: S^T = K Q^T, masking bias,
+// online softmax; leaves P^T (fp16, B-operand layout) in pb. after_mfma(i)
+// runs after the i-th of the 2*D/16 score MFMAs. Element e2 of
+// score subtile kt is key kt*32 + 8*(e2/4) + 4*hh + e2%4 of the tile.
+template <int D, bool SCALED, bool GENERAL, typename Hook>
+__device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t, WaveState<D>& ws,
+                                           const uint16_t* kl, const float* ksc, const float* vsc, int k_lane,
+                                           int r, int hh, int my_qb, int qb_lo, int n_qbt, f16x8 (&pb)[4],
+                                           Hook&& after_mfma) {
   using L = Layout<D>;
   constexpr int NKS = D / 16;
   constexpr int NDT = D / 32;
@@ -352,13 +436,14 @@ __device__ __forceinline__ void compute_tile(const AttnParams& p, const TileInfo
         ka[i % PF] = *reinterpret_cast<const bf16x8*>(kl + k_lane + ((i + PF) / NKS) * 32 * L::KS +
                                                       ((i + PF) % NKS) * 16);
       s[i / NKS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.qf[i % NKS], s[i / NKS], 0, 0, 0);
+      after_mfma(i);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // ---- masking bias: one extra k-step. A[key][slot] in lane (key, hh = 0)
+  // ---- masking bias: one extra k-step. Lane (key, hh) supplies A[key][slot]
+  // for slots 8*hh .. 8*hh+7 (slot = q-block inside the workgroup's rows)
   if (GENERAL || t.n_valid < BK) {
-    const AttnSegment& sg = p.seg[t.seg];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int key = kt * 32 + r;
@@ -366,24 +451,23 @@ __device__ __forceinline__ void compute_tile(const AttnParams& p, const TileInfo
       bf16x8 a;
 #pragma unroll
       for (int j = 0; j < 8; ++j) a[j] = (__bf16)0.0f;
-      if (hh == 0) {
-        if (GENERAL) {
-          const int kb = sg.kb_start + (t.key0 + min(key, t.n_valid - 1)) / p.block_k;
+      if (GENERAL) {
+        const int kb = t.kb_start + (t.key0 + min(key, t.n_valid - 1)) / p.block_k;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const bool keep = kvalid && j < n_qbt && p.mask[(int64_t)(qb_lo + j) * p.n_kb + kb] != 0;
-            a[j] = keep ? (__bf16)0.0f : (__bf16)MASK_BIAS;
-          }
-        } else {
-          a[0] = kvalid ? (__bf16)0.0f : (__bf16)MASK_BIAS;
+        for (int j = 0; j < 8; ++j) {
+          const int slot = 8 * hh + j;
+          const bool keep = kvalid && slot < n_qbt && p.mask[(int64_t)(qb_lo + slot) * p.n_kb + kb] != 0;
+          a[j] = keep ? (__bf16)0.0f : (__bf16)MASK_BIAS;
         }
+      } else if (hh == 0) {
+        a[0] = kvalid ? (__bf16)0.0f : (__bf16)MASK_BIAS;
       }
       s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.qsel, s[kt], 0, 0, 0);
     }
     if (GENERAL) {
       // does any kept key of this tile reach this lane's query row?
-      const int kb_lo = sg.kb_start + t.key0 / p.block_k;
-      const int kb_hi = sg.kb_start + (t.key0 + t.n_valid - 1) / p.block_k;
+      const int kb_lo = t.kb_start + t.key0 / p.block_k;
+      const int kb_hi = t.kb_start + (t.key0 + t.n_valid - 1) / p.block_k;
       for (int kb = kb_lo; kb <= kb_hi; ++kb) ws.seen |= p.mask[(int64_t)my_qb * p.n_kb + kb] != 0;
     }
   }
@@ -428,7 +512,6 @@ __device__ __forceinline__ void compute_tile(const AttnParams& p, const TileInfo
   f16x2 ones;
   ones[0] = (_Float16)1.0f;
   ones[1] = (_Float16)1.0f;
-  f16x8 pb[4];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     float pv[16];
@@ -463,29 +546,42 @@ __device__ __forceinline__ void compute_tile(const AttnParams& p, const TileInfo
       }
     }
   }
+}
 
-  // ---- O^T += V^T P^T (transposed reads of the row-major fp16 V tile)
-  {
-    constexpr int NPV = 4 * NDT;
-    f16x8 va[PF];
+// Second half of a tile: O^T += V^T P^T (transposed reads of the row-major
+// fp16 V tile).
+template <int D, int PF>
+__device__ __forceinline__ void pv_tile(WaveState<D>& ws, const uint16_t* vl, int v_lane, const f16x8 (&pb)[4]) {
+  constexpr int NPV = 4 * (D / 32);
+  f16x8 va[PF];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) va[i] = read_vt<D>(vl, v_lane, i / 4, i % 4);
+  for (int i = 0; i < PF; ++i) va[i] = read_vt<D>(vl, v_lane, i / 4, i % 4);
 #pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      const f16x8 a = va[i % PF];
-      if (i + PF < NPV) va[i % PF] = read_vt<D>(vl, v_lane, (i + PF) / 4, (i + PF) % 4);
-      ws.o[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[i % 4], ws.o[i / 4], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int i = 0; i < NPV; ++i) {
+    const f16x8 a = va[i % PF];
+    if (i + PF < NPV) va[i % PF] = read_vt<D>(vl, v_lane, (i + PF) / 4, (i + PF) % 4);
+    ws.o[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[i % 4], ws.o[i / 4], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
+// Query-block bits (relative to the workgroup's first q-block) that wave w's
+// 32 rows touch; 0 for a wave whose rows all lie past n_q.
+__device__ __forceinline__ uint32_t wave_qbits(const AttnParams& p, int q_lo, int qb_lo, int w) {
+  const int r0 = q_lo + 32 * w;
+  if (r0 >= p.n_q) return 0u;
+  const int r1 = min(p.n_q, r0 + 32) - 1;
+  const int b0 = r0 / p.block_q - qb_lo, b1 = r1 / p.block_q - qb_lo;
+  return ((2u << b1) - 1u) & ~((1u << b0) - 1u);
+}
+
 template <int D, bool SCALED, bool GENERAL>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   using L = Layout<D>;
   __shared__ __attribute__((aligned(16))) Smem<D> sm;
   constexpr int NKS = D / 16;
   constexpr int NDT = D / 32;
+  constexpr int PF_PV = SCALED ? 2 : 4;
 
   // ---- XCD-aware work mapping: consecutive items on one XCD
   const int G = gridDim.x, b = blockIdx.x;
@@ -504,6 +600,10 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
   const int g16 = lane >> 4;
   const int q_row = qt * BQ + wave * 32 + r;
   const bool q_ok = q_row < p.n_q;
+  // Waves NW/2.. run half a tile behind the others: they multiply the
+  // previous tile's P with V first, so on every SIMD one wave's softmax
+  // overlaps the other's matrix work.
+  const bool lagging = wave >= NW / 2;
 
   // q-block range of this workgroup (mask lookups and bias slots)
   const int q_lo = qt * BQ;
@@ -520,10 +620,11 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
       uint4 w = q_ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
       ws.qf[ks] = __builtin_bit_cast(bf16x8, w);
     }
-    // bias selector: slot = the lane's q-block inside the tile (general masks) or slot 0
+    // bias selector: slot = the lane's q-block inside the workgroup (general
+    // masks) or slot 0; slot s sits in lane half s/8, element s%8
     const int slot = GENERAL ? my_qb - qb_lo : 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ws.qsel[j] = (hh == 0 && j == slot) ? (__bf16)1.0f : (__bf16)0.0f;
+    for (int j = 0; j < 8; ++j) ws.qsel[j] = (8 * hh + j == slot) ? (__bf16)1.0f : (__bf16)0.0f;
   }
 #pragma unroll
   for (int i = 0; i < NDT; ++i)
@@ -539,33 +640,43 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
   // 16*(g16&1) + 4*(s16&3) inside each 32-column tile
   const int v_lane = (4 * hh + (s16 >> 2)) * L::VS + 16 * (g16 & 1) + 4 * (s16 & 3);
 
-  int buf = 0;
   Stage<D> st;
   LoadPlan<D> plan;
   make_plan<D>(plan, p.n_heads * D);
+  // q-block bits of every wave of the workgroup (tile compaction)
+  uint32_t wq[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) wq[w] = wave_qbits(p, q_lo, qb_lo, w);
 
 #pragma unroll 1
   for (int cbase = 0; cbase < p.n_tiles; cbase += LIST_CAP) {
-    // ---- compact the kept tiles of this chunk into sm.list (order preserved)
+    // ---- compact the kept tiles of this pass into sm.list (order preserved),
+    // with the set of waves that have a kept (q-block, k-block) pair in each
     const int ncand = min(LIST_CAP, p.n_tiles - cbase);
-    bool keep[2];
+    uint32_t wmk[2];
+    TileInfo ti[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = 2 * tid + i;
-      keep[i] = false;
+      wmk[i] = 0;
       if (c < ncand) {
         const TileInfo t = tile_info(p, cbase + c);
+        ti[i] = t;
         const AttnSegment& sg = p.seg[t.seg];
         const int kb_lo = sg.kb_start + t.key0 / p.block_k;
         const int kb_hi = sg.kb_start + (t.key0 + t.n_valid - 1) / p.block_k;
-        bool any = false;
-        for (int qb = qb_lo; qb <= qb_hi && !any; ++qb)
-          for (int kb = kb_lo; kb <= kb_hi; ++kb) any |= p.mask[(int64_t)qb * p.n_kb + kb] != 0;
-        keep[i] = any;
+        uint32_t qbits = 0;
+        for (int qb = qb_lo; qb <= qb_hi; ++qb) {
+          bool any = false;
+          for (int kb = kb_lo; kb <= kb_hi && !any; ++kb) any = p.mask[(int64_t)qb * p.n_kb + kb] != 0;
+          if (any) qbits |= 1u << (qb - qb_lo);
+        }
+#pragma unroll
+        for (int w = 0; w < NW; ++w) wmk[i] |= (qbits & wq[w]) ? (1u << w) : 0u;
       }
     }
-    const uint64_t b0 = __ballot(keep[0]);
-    const uint64_t b1 = __ballot(keep[1]);
+    const uint64_t b0 = __ballot(wmk[0] != 0);
+    const uint64_t b1 = __ballot(wmk[1] != 0);
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     if (lane == 0) sm.wave_count[wave] = __popcll(b0) + __popcll(b1);
     __syncthreads();
@@ -578,37 +689,59 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnParams p) {
     }
     {
       int pos = base + __popcll(b0 & lt) + __popcll(b1 & lt);
-      if (keep[0]) sm.list[pos++] = (uint16_t)(2 * tid);
-      if (keep[1]) sm.list[pos] = (uint16_t)(2 * tid + 1);
+      if (wmk[0]) sm.desc[pos++] = pack_desc(ti[0], wmk[0]);
+      if (wmk[1]) sm.desc[pos] = pack_desc(ti[1], wmk[1]);
     }
     __syncthreads();
     if (total == 0) continue;
 
-    // ---- prologue: first kept tile into LDS
-    {
-      const TileInfo t = tile_info(p, cbase + sm.list[0]);
-      issue_tile<D, SCALED>(p, t, head, st, sm, buf, plan);
-      commit_tile<D, SCALED>(p, t, st, sm, buf);
-    }
+    // ---- prologue: first kept tile into K buffer 0 / V buffer 0
+    TileRef tn = tile_ref(p, sm.desc[0]);
+    issue_tile<D, SCALED>(p, tn, head, st, sm, 0, plan);
+    commit_tile<D, SCALED>(tn, st, sm, 0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    TileInfo tn = tile_info(p, cbase + sm.list[0]);
+    // Tile i lives in K buffer i%2 (and scale slot i%2) and V buffer i%3.
+    // During step i the loads of tile i+1 go to K buffer (i+1)%2 and, at the
+    // end of the step, V buffer (i+1)%3, while the leading waves read tile i
+    // and the lagging ones tiles i-1 (V only) and i.
+    f16x8 pb[4];
+    bool pending = false;   // lagging waves: P of the previous tile awaits its P.V
+    int kbuf = 0, vbuf = 0, vprev = NVBUF - 1;
 #pragma unroll 1
     for (int it = 0; it < total; ++it) {
-      const TileInfo t = tn;
+      const TileRef t = tn;
       const bool has_next = it + 1 < total;
-      if (has_next) {
-        tn = tile_info(p, cbase + sm.list[it + 1]);
-        issue_tile<D, SCALED>(p, tn, head, st, sm, buf ^ 1, plan);
+      const int knext = kbuf ^ 1;
+      const int vnext = (vbuf + 1 == NVBUF) ? 0 : vbuf + 1;
+      if (has_next) tn = tile_ref(p, sm.desc[it + 1]);
+      if (lagging && pending) pv_tile<D, PF_PV>(ws, sm.v[vprev], v_lane, pb);
+      pending = false;
+      if ((t.wmask >> wave) & 1) {
+        // the next tile's loads ride on the score MFMAs
+        constexpr int STRIDE = (2 * NKS) / TileLoad<D>::NPART;
+        qk_softmax<D, SCALED, GENERAL>(p, t, ws, sm.k[kbuf], sm.ksc[kbuf], sm.vsc[kbuf], k_lane, r, hh, my_qb,
+                                       qb_lo, n_qbt, pb, [&](int i) {
+                                         if (has_next && i % STRIDE == 0 && i / STRIDE < TileLoad<D>::NPART)
+                                           issue_part<D, SCALED>(p, tn, head, st, sm, knext, plan, i / STRIDE);
+                                       });
+        if (lagging)
+          pending = true;
+        else
+          pv_tile<D, PF_PV>(ws, sm.v[vbuf], v_lane, pb);
+      } else if (has_next) {
+        issue_tile<D, SCALED>(p, tn, head, st, sm, knext, plan);
       }
-      compute_tile<D, SCALED, GENERAL>(p, t, ws, sm.k[buf], sm.v[buf], sm.ksc[buf], sm.vsc[buf], k_lane, v_lane,
-                                       r, hh, my_qb, qb_lo, n_qbt);
-      if (has_next) commit_tile<D, SCALED>(p, tn, st, sm, buf ^ 1);
+      if (has_next) commit_tile<D, SCALED>(tn, st, sm, knext, vnext);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      buf ^= 1;
+      vprev = vbuf;
+      kbuf = knext;
+      vbuf = vnext;
     }
+    // the last tile's V buffer stays untouched until the next pass's barriers
+    if (pending) pv_tile<D, PF_PV>(ws, sm.v[vprev], v_lane, pb);
   }
 
   // ---- finalise
@@ -649,8 +782,10 @@ template <int D>
 hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
   bool scaled = false;
   for (int s = 0; s < p.n_segs; ++s) scaled |= p.seg[s].is_int8 && p.seg[s].len > 0;
-  // mask blocks finer than the 128-row x 64-key tile need the per-q-block bias
-  const bool general = p.block_q < BQ || p.block_k < BK;
+  // A wave's 32 rows lie in one q-block when block_q >= 32, and a 64-key tile
+  // in one k-block when block_k >= 64: then a wave either skips a tile or sees
+  // all of its keys. Finer mask blocks need the per-q-block bias.
+  const bool general = p.block_q < 32 || p.block_k < BK;
   if (scaled) return general ? launch<D, true, true>(p, stream) : launch<D, true, false>(p, stream);
   return general ? launch<D, false, true>(p, stream) : launch<D, false, false>(p, stream);
 }

@@ -173,6 +173,8 @@ int fill_attn_params(const void* q, int32_t n_q, const sdit_kv_segment* segs, in
   if (head_dim != 64 && head_dim != 128)
     return fail(SDIT_ERR_UNSUPPORTED, "attn_fwd: head_dim %d not in {64, 128}", head_dim);
   if (n_heads < 1) return fail(SDIT_ERR_INVALID, "attn_fwd: n_heads %d < 1", n_heads);
+  // a key tile's rows are addressed with 32-bit offsets from its first row
+  if (n_heads > 65536) return fail(SDIT_ERR_UNSUPPORTED, "attn_fwd: n_heads %d > 65536", n_heads);
   if (n_q < 0) return fail(SDIT_ERR_INVALID, "attn_fwd: n_q %d < 0", n_q);
   if (!valid_block(block_q) || !valid_block(block_k))
     return fail(SDIT_ERR_UNSUPPORTED, "attn_fwd: block sizes %d x %d not in {16, 32, 64, 128}", block_q, block_k);
@@ -204,7 +206,8 @@ int fill_attn_params(const void* q, int32_t n_q, const sdit_kv_segment* segs, in
     tiles += (sg.len + sdit::kAttnBK - 1) / sdit::kAttnBK;
     kbs += ceil_div(sg.len, block_k);
   }
-  if (tiles > (1 << 24)) return fail(SDIT_ERR_UNSUPPORTED, "attn_fwd: more than 2^30 keys");
+  if (tiles > (1 << 24))
+    return fail(SDIT_ERR_UNSUPPORTED, "attn_fwd: more than 2^24 key tiles of %d keys", sdit::kAttnBK);
   const int n_qb = ceil_div(n_q, block_q);
   const int n_qt = ceil_div(n_q, sdit::kAttnBQ);
   if ((int64_t)n_qt * n_heads > INT32_MAX / 2) return fail(SDIT_ERR_INVALID, "attn_fwd: grid too large");

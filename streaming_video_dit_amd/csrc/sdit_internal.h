@@ -61,7 +61,7 @@ struct AttnParams {
   int32_t block_k;
   float scale_log2;    // softmax_scale * log2(e)
 };
-constexpr int kAttnBQ = 128;  // query rows per workgroup
+constexpr int kAttnBQ = 256;  // query rows per workgroup
 constexpr int kAttnBK = 64;   // keys per pipeline stage
 hipError_t launch_attn_fwd(const AttnParams& p, int head_dim, hipStream_t stream);
 

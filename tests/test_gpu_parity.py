@@ -196,6 +196,12 @@ CASES = {
     "d64_b32_int8": (100, 1, 64, [129, 100], ["int8", "bf16"], 32, 32, 0.5, (1,)),
     "one_query": (1, 4, 128, [5, 1], ["bf16", "bf16"], 16, 16, 1.0, ()),
     "eight_segments": (130, 2, 128, [1, 63, 64, 65, 0, 128, 3, 130], ["bf16", "int8"] * 4, 128, 64, 0.8, ()),
+    # 16-row q-blocks: all 16 bias slots of a 256-row workgroup, a ragged second one
+    "d128_b16_sixteen_slots": (300, 2, 128, [90, 300], ["bf16", "bf16"], 16, 32, 0.5, (3, 12)),
+    "d64_b16_int8_slots": (270, 2, 64, [100, 270], ["int8", "bf16"], 16, 64, 0.6, (9,)),
+    # 32-row q-blocks: waves skip the tiles their rows drop, no bias needed
+    "d128_b32_wave_skip": (520, 2, 128, [256, 520], ["bf16", "bf16"], 32, 64, 0.3, (5,)),
+    "d128_b32_int8_wave_skip": (333, 2, 128, [160, 333], ["int8", "bf16"], 32, 128, 0.4, (0, 7)),
 }
 
 
@@ -246,16 +252,19 @@ def test_nan_in_skipped_tiles_never_reaches_the_output():
     assert_attn_close(out_p, lse_p, O, LSE, "poisoned")
 
 
-def test_rows_whose_first_tiles_are_fully_masked():
-    # 32-row q-blocks inside one 128-row tile: q-block 0 skips the first three
-    # 64-key tiles that its neighbours keep, so its rows meet whole tiles of
-    # -1e30-biased scores before any visible key. Their output must be the
-    # attention over the later keys only (no overflow from the bias).
-    q, segs, mask = _rand_case(21, 128, 2, 128, [512], ["bf16"], 32, 64)
+@pytest.mark.parametrize("bq", [32, 16])
+def test_rows_whose_first_tiles_are_fully_masked(bq):
+    # q-block 0 drops the first three 64-key tiles that its neighbours keep.
+    # With 32-row q-blocks the wave holding those rows skips the tiles; with
+    # 16-row q-blocks the same wave also holds rows that keep them, so the
+    # rows of q-block 0 meet whole tiles of -1e30-biased scores before any
+    # visible key. Either way their output must be the attention over the
+    # later keys only (no overflow from the bias).
+    q, segs, mask = _rand_case(21, 128, 2, 128, [512], ["bf16"], bq, 64)
     mask[0, :3] = 0
     mask[2, 5:] = 0
-    out, lse = run_attn(q, segs, mask, 32, 64)
-    O, LSE = oracle.attention(q, segs, mask, 32, 64)
+    out, lse = run_attn(q, segs, mask, bq, 64)
+    O, LSE = oracle.attention(q, segs, mask, bq, 64)
     assert not np.isnan(lse).any()
     assert_attn_close(out, lse, O, LSE, "first tiles masked")
 
