@@ -403,13 +403,14 @@ struct WaveState {
 
 // First half of a 64-key tile for one wave: S^T = K Q^T, masking bias,
 // online softmax; leaves P^T (fp16, B-operand layout) in pb. after_mfma(i)
-// runs after the i-th of the 2*D/16 score MFMAs. Element e2 of
+// runs after the i-th of the 2*D/16 score MFMAs, after_scores() after the
+// last one. Element e2 of
 // score subtile kt is key kt*32 + 8*(e2/4) + 4*hh + e2%4 of the tile.
-template <int D, bool SCALED, bool GENERAL, typename Hook>
+template <int D, bool SCALED, bool GENERAL, typename Hook, typename Tail>
 __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t, WaveState<D>& ws,
                                            const uint16_t* kl, const float* ksc, const float* vsc, int k_lane,
                                            int r, int hh, int my_qb, int qb_lo, int n_qbt, f16x8 (&pb)[4],
-                                           Hook&& after_mfma) {
+                                           Hook&& after_mfma, Tail&& after_scores) {
   using L = Layout<D>;
   constexpr int NKS = D / 16;
   constexpr int NDT = D / 32;
@@ -440,6 +441,7 @@ __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  after_scores();
 
   // ---- masking bias: one extra k-step. Lane (key, hh) supplies A[key][slot]
   // for slots 8*hh .. 8*hh+7 (slot = q-block inside the workgroup's rows)
@@ -719,13 +721,23 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       if (lagging && pending) pv_tile<D, PF_PV>(ws, sm.v[vprev], v_lane, pb);
       pending = false;
       if ((t.wmask >> wave) & 1) {
-        // the next tile's loads ride on the score MFMAs
-        constexpr int STRIDE = (2 * NKS) / TileLoad<D>::NPART;
-        qk_softmax<D, SCALED, GENERAL>(p, t, ws, sm.k[kbuf], sm.ksc[kbuf], sm.vsc[kbuf], k_lane, r, hh, my_qb,
-                                       qb_lo, n_qbt, pb, [&](int i) {
-                                         if (has_next && i % STRIDE == 0 && i / STRIDE < TileLoad<D>::NPART)
-                                           issue_part<D, SCALED>(p, tn, head, st, sm, knext, plan, i / STRIDE);
-                                       });
+        // The next tile's register loads ride on the score MFMAs; its
+        // direct-to-LDS loads follow the last score MFMA (the compiler waits
+        // for every LDS read in flight after one of those, which would stall
+        // the operand prefetch inside the MFMA sequence).
+        constexpr int KM = TileLoad<D>::KMAX;
+        constexpr int STRIDE = (2 * NKS) / (TileLoad<D>::NPART - KM);
+        qk_softmax<D, SCALED, GENERAL>(
+            p, t, ws, sm.k[kbuf], sm.ksc[kbuf], sm.vsc[kbuf], k_lane, r, hh, my_qb, qb_lo, n_qbt, pb,
+            [&](int i) {
+              if (has_next && i % STRIDE == 0 && KM + i / STRIDE < TileLoad<D>::NPART)
+                issue_part<D, SCALED>(p, tn, head, st, sm, knext, plan, KM + i / STRIDE);
+            },
+            [&]() {
+              if (has_next)
+#pragma unroll
+                for (int j = 0; j < KM; ++j) issue_part<D, SCALED>(p, tn, head, st, sm, knext, plan, j);
+            });
         if (lagging)
           pending = true;
         else
