@@ -111,13 +111,20 @@ struct Layout {
   static constexpr int VS = D + 32;            // V row stride (fp16 elements)
   static constexpr int K_CH = KS / 8;          // chunks per padded K row
   static constexpr int K_BLKS = BK * K_CH / 64;  // 64-lane direct-load blocks per K tile
-  static constexpr int VCH = BK * CPR / NT;    // bf16 V chunks staged per thread
-  static constexpr int I8_THREADS = BK * (D / 16);  // threads moving 16 int8 codes of K and of V
-  static constexpr int I8CH = I8_THREADS >= NT ? I8_THREADS / NT : 1;
-  static constexpr int SR = VCH > 2 * I8CH ? VCH : 2 * I8CH;
   static_assert(BK * K_CH % 64 == 0, "K tile must be whole 64-lane blocks");
-  static_assert(VCH >= 1 && BK * CPR % NT == 0, "V tile must be whole chunks per thread");
-  static_assert(I8_THREADS % NT == 0 || I8_THREADS < NT, "int8 tile split");
+};
+
+// Who moves a tile: the first LW waves of the workgroup (LT threads).
+template <int D, int LW>
+struct Loader {
+  static constexpr int LT = LW * 64;
+  static constexpr int VCH = BK * Layout<D>::CPR / LT;  // bf16 V chunks staged per thread
+  static constexpr int I8_THREADS = BK * (D / 16);      // threads moving 16 int8 codes of K and of V
+  static constexpr int I8CH = I8_THREADS >= LT ? I8_THREADS / LT : 1;
+  static constexpr int SR = VCH > 2 * I8CH ? VCH : 2 * I8CH;
+  static constexpr int KMAX = (Layout<D>::K_BLKS + LW - 1) / LW;   // direct-load blocks per wave
+  static_assert(VCH >= 1 && BK * Layout<D>::CPR % LT == 0, "V tile must be whole chunks per thread");
+  static_assert(I8_THREADS % LT == 0 || I8_THREADS < LT, "int8 tile split");
 };
 
 template <int D>
@@ -219,29 +226,29 @@ __device__ __forceinline__ uint4 i8x8_to_f16x8(uint32_t w0, uint32_t w1) {
 // Registers holding the register-staged part of one tile between its global
 // load and its LDS store. bf16 tiles: VCH chunks of 8 V values. int8 tiles:
 // I8CH chunks of 16 K codes, then I8CH chunks of 16 V codes.
-template <int D>
+template <int D, int LW>
 struct Stage {
-  uint4 r[Layout<D>::SR];
+  uint4 r[Loader<D, LW>::SR];
   float ks, vs;
 };
 
 // Per-thread load geometry, fixed for the whole kernel: element offsets (from
 // a tile's first row, head included) of every chunk this thread moves.
-template <int D>
+template <int D, int LW>
 struct LoadPlan {
-  static constexpr int KMAX = (Layout<D>::K_BLKS + NW - 1) / NW;   // direct-load blocks per wave
-  int k_off[KMAX];   // bf16 K, padded-tile block wave + NW*i (padding chunks reload chunk 0)
-  int v_off;         // bf16 V chunk j adds j * (NT / CPR) rows
-  int i8_off;        // int8 K/V chunk j adds j * (NT / (D/16)) rows
+  static constexpr int KMAX = Loader<D, LW>::KMAX;
+  int k_off[KMAX];   // bf16 K, padded-tile block wave + LW*i (padding chunks reload chunk 0)
+  int v_off;         // bf16 V chunk j adds j * (LT / CPR) rows
+  int i8_off;        // int8 K/V chunk j adds j * (LT / (D/16)) rows
 };
 
-template <int D>
-__device__ __forceinline__ void make_plan(LoadPlan<D>& pl, int row_stride) {
+template <int D, int LW>
+__device__ __forceinline__ void make_plan(LoadPlan<D, LW>& pl, int row_stride) {
   using L = Layout<D>;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-  for (int i = 0; i < LoadPlan<D>::KMAX; ++i) {
-    const int lin = (wave + NW * i) * 64 + lane;
+  for (int i = 0; i < LoadPlan<D, LW>::KMAX; ++i) {
+    const int lin = (wave + LW * i) * 64 + lane;
     const int row = lin / L::K_CH, pc = lin % L::K_CH;
     pl.k_off[i] = row * row_stride + (pc < L::CPR ? pc : 0) * 8;
   }
@@ -257,18 +264,20 @@ __device__ __forceinline__ void make_plan(LoadPlan<D>& pl, int row_stride) {
 // V codes into registers, then the per-key scales. Rows past the segment end
 // are loaded from its last row: their scores get the -1e30 bias, so their
 // probabilities are exactly 0 and any finite data there is harmless.
-template <int D>
+template <int D, int LW>
 struct TileLoad {
-  static constexpr int KMAX = LoadPlan<D>::KMAX;
-  static constexpr int NB16 = KMAX + Layout<D>::VCH;
-  static constexpr int NI8 = 2 * Layout<D>::I8CH + 1;
+  static constexpr int KMAX = Loader<D, LW>::KMAX;
+  static constexpr int NB16 = KMAX + Loader<D, LW>::VCH;
+  static constexpr int NI8 = 2 * Loader<D, LW>::I8CH + 1;
   static constexpr int NPART = NB16 > NI8 ? NB16 : NI8;
 };
 
-template <int D, bool SCALED>
-__device__ __forceinline__ void issue_part(const AttnParams& p, const TileRef& t, int head, Stage<D>& st,
-                                           Smem<D>& sm, int kbuf, const LoadPlan<D>& pl, int j) {
+template <int D, bool SCALED, int LW>
+__device__ __forceinline__ void issue_part(const AttnParams& p, const TileRef& t, int head, Stage<D, LW>& st,
+                                           Smem<D>& sm, int kbuf, const LoadPlan<D, LW>& pl, int j) {
   using L = Layout<D>;
+  using LD = Loader<D, LW>;
+  constexpr int LT = LD::LT;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int row_stride = p.n_heads * D;   // elements between consecutive tokens
@@ -277,8 +286,8 @@ __device__ __forceinline__ void issue_part(const AttnParams& p, const TileRef& t
   if (!SCALED || !t.is_int8) {
     const uint16_t* kb = (const uint16_t*)t.k + base;
     const uint16_t* vb = (const uint16_t*)t.v + base;
-    if (j < TileLoad<D>::KMAX) {
-      const int blk = wave + NW * j;
+    if (j < TileLoad<D, LW>::KMAX) {
+      const int blk = wave + LW * j;
       if (blk < L::K_BLKS) {
         int off = pl.k_off[j];
         if (ragged) {
@@ -288,9 +297,9 @@ __device__ __forceinline__ void issue_part(const AttnParams& p, const TileRef& t
         }
         __builtin_amdgcn_global_load_lds((const void*)(kb + off), (lds_void*)(sm.k[kbuf] + blk * 64 * 8), 16, 0, 0);
       }
-    } else if (j < TileLoad<D>::NB16) {
-      const int jv = j - TileLoad<D>::KMAX;
-      constexpr int RSTEP = NT / L::CPR;
+    } else if (j < TileLoad<D, LW>::NB16) {
+      const int jv = j - TileLoad<D, LW>::KMAX;
+      constexpr int RSTEP = LT / L::CPR;
       int off = pl.v_off + jv * RSTEP * row_stride;
       if (ragged) off = min(tid / L::CPR + jv * RSTEP, t.n_valid - 1) * row_stride + (tid % L::CPR) * 8;
       st.r[jv] = *reinterpret_cast<const uint4*>(vb + off);
@@ -302,18 +311,18 @@ __device__ __forceinline__ void issue_part(const AttnParams& p, const TileRef& t
   } else {
     const int8_t* kb = (const int8_t*)t.k + base;
     const int8_t* vb = (const int8_t*)t.v + base;
-    if (j < 2 * L::I8CH) {
-      if (L::I8_THREADS >= NT || tid < L::I8_THREADS) {
-        const int ji = j % L::I8CH;
-        constexpr int RSTEP = NT / (D / 16);
+    if (j < 2 * LD::I8CH) {
+      if (LD::I8_THREADS >= LT || tid < LD::I8_THREADS) {
+        const int ji = j % LD::I8CH;
+        constexpr int RSTEP = LT / (D / 16);
         int off = pl.i8_off + ji * RSTEP * row_stride;
         if (ragged) off = min(tid / (D / 16) + ji * RSTEP, t.n_valid - 1) * row_stride + (tid % (D / 16)) * 16;
-        if (j < L::I8CH)
+        if (j < LD::I8CH)
           st.r[ji] = *reinterpret_cast<const uint4*>(kb + off);
         else
-          st.r[L::I8CH + ji] = *reinterpret_cast<const uint4*>(vb + off);
+          st.r[LD::I8CH + ji] = *reinterpret_cast<const uint4*>(vb + off);
       }
-    } else if (j == 2 * L::I8CH && tid < BK) {
+    } else if (j == 2 * LD::I8CH && tid < BK) {
       // keys past the segment end keep a positive K multiplier so their bias stays -1e30
       const bool ok = tid < t.n_valid;
       const int64_t si = (int64_t)(t.key0 + min(tid, t.n_valid - 1)) * p.n_heads + head;
@@ -324,35 +333,36 @@ __device__ __forceinline__ void issue_part(const AttnParams& p, const TileRef& t
   }
 }
 
-template <int D, bool SCALED>
-__device__ __forceinline__ void issue_tile(const AttnParams& p, const TileRef& t, int head, Stage<D>& st,
-                                           Smem<D>& sm, int kbuf, const LoadPlan<D>& pl) {
+template <int D, bool SCALED, int LW>
+__device__ __forceinline__ void issue_tile(const AttnParams& p, const TileRef& t, int head, Stage<D, LW>& st,
+                                           Smem<D>& sm, int kbuf, const LoadPlan<D, LW>& pl) {
 #pragma unroll
-  for (int j = 0; j < TileLoad<D>::NPART; ++j) issue_part<D, SCALED>(p, t, head, st, sm, kbuf, pl, j);
+  for (int j = 0; j < TileLoad<D, LW>::NPART; ++j) issue_part<D, SCALED, LW>(p, t, head, st, sm, kbuf, pl, j);
 }
 
 // Finish tile t: register-staged V (and int8 K) into LDS buffers vbuf (kbuf),
 // scaled-path multipliers into slot kbuf.
-template <int D, bool SCALED>
-__device__ __forceinline__ void commit_tile(const TileRef& t, const Stage<D>& st, Smem<D>& sm, int kbuf,
+template <int D, bool SCALED, int LW>
+__device__ __forceinline__ void commit_tile(const TileRef& t, const Stage<D, LW>& st, Smem<D>& sm, int kbuf,
                                             int vbuf) {
   using L = Layout<D>;
+  using LD = Loader<D, LW>;
   const int tid = threadIdx.x;
   if (!SCALED || !t.is_int8) {
 #pragma unroll
-    for (int j = 0; j < L::VCH; ++j) {
-      const int lin = tid + j * NT;
+    for (int j = 0; j < LD::VCH; ++j) {
+      const int lin = tid + j * LD::LT;
       const int row = lin / L::CPR, c = lin % L::CPR;
       *reinterpret_cast<uint4*>(sm.v[vbuf] + row * L::VS + c * 8) = bf16x8_to_f16x8(st.r[j]);
     }
-  } else if (L::I8_THREADS >= NT || tid < L::I8_THREADS) {
+  } else if (LD::I8_THREADS >= LD::LT || tid < LD::I8_THREADS) {
 #pragma unroll
-    for (int j = 0; j < L::I8CH; ++j) {
-      const int lin = tid + j * NT;
+    for (int j = 0; j < LD::I8CH; ++j) {
+      const int lin = tid + j * LD::LT;
       const int row = lin / (D / 16), c16 = lin % (D / 16);
       uint16_t* kr = sm.k[kbuf] + row * L::KS + 16 * c16;
       uint16_t* vr = sm.v[vbuf] + row * L::VS + 16 * c16;
-      const uint4 kc = st.r[j], vc = st.r[L::I8CH + j];
+      const uint4 kc = st.r[j], vc = st.r[LD::I8CH + j];
       *reinterpret_cast<uint4*>(kr) = i8x8_to_bf16x8(kc.x, kc.y);
       *reinterpret_cast<uint4*>(kr + 8) = i8x8_to_bf16x8(kc.z, kc.w);
       *reinterpret_cast<uint4*>(vr) = i8x8_to_f16x8(vc.x, vc.y);
@@ -642,9 +652,15 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   // 16*(g16&1) + 4*(s16&3) inside each 32-column tile
   const int v_lane = (4 * hh + (s16 >> 2)) * L::VS + 16 * (g16 & 1) + 4 * (s16 & 3);
 
-  Stage<D> st;
-  LoadPlan<D> plan;
-  make_plan<D>(plan, p.n_heads * D);
+  // Kernels without int8 segments leave all loading and staging to the
+  // leading waves (which otherwise wait at the barrier for the lagging
+  // ones); kernels with int8 segments share it over all waves (the staged
+  // int8 tiles need the registers).
+  constexpr int LW = SCALED ? NW : NW / 2;
+  const bool loader = wave < LW;
+  Stage<D, LW> st;
+  LoadPlan<D, LW> plan;
+  make_plan<D, LW>(plan, p.n_heads * D);
   // q-block bits of every wave of the workgroup (tile compaction)
   uint32_t wq[NW];
 #pragma unroll
@@ -699,8 +715,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
 
     // ---- prologue: first kept tile into K buffer 0 / V buffer 0
     TileRef tn = tile_ref(p, sm.desc[0]);
-    issue_tile<D, SCALED>(p, tn, head, st, sm, 0, plan);
-    commit_tile<D, SCALED>(tn, st, sm, 0, 0);
+    if (loader) {
+      issue_tile<D, SCALED, LW>(p, tn, head, st, sm, 0, plan);
+      commit_tile<D, SCALED, LW>(tn, st, sm, 0, 0);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -725,27 +743,27 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         // direct-to-LDS loads follow the last score MFMA (the compiler waits
         // for every LDS read in flight after one of those, which would stall
         // the operand prefetch inside the MFMA sequence).
-        constexpr int KM = TileLoad<D>::KMAX;
-        constexpr int STRIDE = (2 * NKS) / (TileLoad<D>::NPART - KM);
+        constexpr int KM = TileLoad<D, LW>::KMAX;
+        constexpr int STRIDE = (2 * NKS) / (TileLoad<D, LW>::NPART - KM);
         qk_softmax<D, SCALED, GENERAL>(
             p, t, ws, sm.k[kbuf], sm.ksc[kbuf], sm.vsc[kbuf], k_lane, r, hh, my_qb, qb_lo, n_qbt, pb,
             [&](int i) {
-              if (has_next && i % STRIDE == 0 && KM + i / STRIDE < TileLoad<D>::NPART)
-                issue_part<D, SCALED>(p, tn, head, st, sm, knext, plan, KM + i / STRIDE);
+              if (loader && has_next && i % STRIDE == 0 && KM + i / STRIDE < TileLoad<D, LW>::NPART)
+                issue_part<D, SCALED, LW>(p, tn, head, st, sm, knext, plan, KM + i / STRIDE);
             },
             [&]() {
-              if (has_next)
+              if (loader && has_next)
 #pragma unroll
-                for (int j = 0; j < KM; ++j) issue_part<D, SCALED>(p, tn, head, st, sm, knext, plan, j);
+                for (int j = 0; j < KM; ++j) issue_part<D, SCALED, LW>(p, tn, head, st, sm, knext, plan, j);
             });
         if (lagging)
           pending = true;
         else
           pv_tile<D, PF_PV>(ws, sm.v[vbuf], v_lane, pb);
-      } else if (has_next) {
-        issue_tile<D, SCALED>(p, tn, head, st, sm, knext, plan);
+      } else if (has_next && loader) {
+        issue_tile<D, SCALED, LW>(p, tn, head, st, sm, knext, plan);
       }
-      if (has_next) commit_tile<D, SCALED>(tn, st, sm, knext, vnext);
+      if (has_next && loader) commit_tile<D, SCALED, LW>(tn, st, sm, knext, vnext);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       vprev = vbuf;
