@@ -20,6 +20,10 @@ What it computes, each function citing the passage it follows:
                       (q-block, k-block) tiles of a block mask (FlashVSR
                       deployment notes, Block-Sparse-Attention section: a
                       dense mask must reproduce ordinary SDPA).
+  * ``attention_merge`` combination of attention results over disjoint key
+                      sets by the log-sum-exp identity (the shard merge of
+                      Ulysses / Ring context parallelism, which the Wave
+                      Forcing summary compares against).
 
 Readings of points the pages leave open are stated in each function.
 Parity pinning: every function is pinned by the ``-m "not gpu"`` tests in
@@ -32,11 +36,11 @@ layout the original kernel used is parity unpinned.
 from .bf16 import bf16_to_f64, f64_to_bf16
 from .qknorm_rope3d import rms_norm, rope3d_angles, apply_rope, qknorm_rope3d
 from .kv_quant import kv_quant_int8, kv_dequant
-from .attention import key_block_index, attention, segment_values
+from .attention import key_block_index, attention, segment_values, attention_merge
 
 __all__ = [
     "bf16_to_f64", "f64_to_bf16",
     "rms_norm", "rope3d_angles", "apply_rope", "qknorm_rope3d",
     "kv_quant_int8", "kv_dequant",
-    "key_block_index", "attention", "segment_values",
+    "key_block_index", "attention", "segment_values", "attention_merge",
 ]

@@ -103,3 +103,37 @@ def attention(q_bits: np.ndarray, segments, mask: np.ndarray, block_q: int, bloc
             O[sel, hi, :] = (p @ Vv) / l
             LSE[hi, sel] = m[:, 0] + np.log(l[:, 0])
     return O, LSE
+
+
+def attention_merge(parts):
+    """Combine attention results over disjoint key sets (test infrastructure).
+
+    Source: context-parallel attention of the Ulysses / Ring kind, which the
+    Wave Forcing summary measures Wave Parallelism against: each step attends
+    to one shard of the keys, and the shards' results are combined. Softmax
+    over a disjoint union of key sets A, B satisfies, per query,
+      LSE = log(e^LSE_A + e^LSE_B),
+      o   = e^(LSE_A - LSE) o_A + e^(LSE_B - LSE) o_B,
+    because e^LSE_X is the sum of e^s over X and o_X is the e^s-weighted mean
+    of V over X. Written here for any number of parts with the usual shift by
+    the largest LSE. A part whose query sees no key (LSE = -inf, o = 0) adds
+    nothing; a query that sees no key in any part gets o = 0, LSE = -inf.
+
+    parts: list of (O fp64 [n_q, H, d], LSE fp64 [H, n_q]).
+    Returns (O [n_q, H, d], LSE [H, n_q]) in fp64.
+    """
+    if not parts:
+        raise ValueError("no parts")
+    lses = np.stack([np.asarray(L, dtype=np.float64) for _, L in parts])       # [P, H, n_q]
+    outs = np.stack([np.asarray(O, dtype=np.float64) for O, _ in parts])       # [P, n_q, H, d]
+    m = lses.max(axis=0)                                                       # [H, n_q]
+    seen = np.isfinite(m)
+    shift = np.where(seen, m, 0.0)
+    w = np.exp(lses - shift[None])                                             # exp(-inf) = 0
+    total = w.sum(axis=0)                                                      # [H, n_q]
+    O = np.einsum("phq,pqhd->qhd", w, outs)
+    safe = np.where(seen, total, 1.0)
+    O = np.where(seen.T[:, :, None], O / safe.T[:, :, None], 0.0)
+    LSE = np.where(seen, shift + np.log(safe), -np.inf)
+    return O, LSE
+
