@@ -7,6 +7,11 @@ resident in HBM:
     kv_quant_int8(chunk K), (chunk V)    (int8-cache workload: the steady-state cache write)
     attn_fwd(q, [cache segments..., current chunk])
 
+With --kv-parts N (N > 1) the attention is the split-KV form instead: the
+segments are cut into N groups of consecutive segments, attn_fwd_partial
+runs once per group (fp32 partial O and LSE) and attn_merge combines them;
+the line then also reports the merge kernel against the HBM roofline.
+
 Prints ONE JSON line. ``value`` is effective attention TFLOP/s of the whole
 step (kept-tile FLOPs 4*d*H*sum rows*cols / step time); ``ms_per_step`` is
 the ms/layer/chunk. ``roofline`` reports the attention kernel alone, timed
@@ -32,6 +37,7 @@ import workloads as W  # noqa: E402
 
 METRIC = "attention ms/layer/chunk + effective TFLOP/s (% bf16 MFMA peak), 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
 def _dev(a, torch):
@@ -44,7 +50,7 @@ def _dev(a, torch):
 class Step:
     """Device buffers and the launch sequence of one layer-chunk."""
 
-    def __init__(self, cfg: W.Config, torch, sdit):
+    def __init__(self, cfg: W.Config, torch, sdit, kv_parts: int = 1):
         self.cfg, self.torch, self.sdit = cfg, torch, sdit
         inp = W.make_inputs(cfg)
         self.inp = inp
@@ -77,6 +83,20 @@ class Step:
         segs.append(dict(k=cur_k, v=self.v, len=n, dtype=sdit.SDIT_BF16))
         self.segs = sdit.make_segments(segs)
         self.n_segs = len(segs)
+        # split-KV form: groups of consecutive segments, each with its own mask columns
+        self.kv_parts = kv_parts
+        if kv_parts > 1:
+            if kv_parts > len(segs):
+                raise ValueError(f"--kv-parts {kv_parts} > {len(segs)} segments")
+            cuts = np.linspace(0, len(segs), kv_parts + 1).round().astype(int)
+            starts = np.cumsum([0] + [-(-int(sg["len"]) // cfg.block) for sg in segs])
+            self.groups = []
+            for a, b in zip(cuts[:-1], cuts[1:]):
+                cols = np.ascontiguousarray(inp.mask[:, starts[a]:starts[b]])
+                o = torch.empty((n, H, d), dtype=torch.float32, device="cuda")
+                ls = torch.empty((H, n), dtype=torch.float32, device="cuda")
+                self.groups.append((sdit.make_segments(segs[a:b]), b - a, _dev(cols, torch), o, ls))
+            self.merge_bytes = (kv_parts * (4 * d + 4) + 2 * d + 4) * n * H
         self.q_attn = self.q if cfg.rope else self.q_in
         self.quant_chunk = any(cfg.seg_int8)
         if self.quant_chunk:
@@ -87,7 +107,7 @@ class Step:
         self.flops = W.attn_flops(cfg, inp.mask)
         torch.cuda.synchronize()
 
-    def run(self, ev_before=None, ev_after=None):
+    def run(self, ev_before=None, ev_after=None, ev_merge=None):
         cfg, sdit = self.cfg, self.sdit
         H, d, n = cfg.n_heads, cfg.head_dim, cfg.n_q
         if cfg.rope:
@@ -99,7 +119,14 @@ class Step:
             sdit.kv_quant_int8(self.v, self.cv, self.sv, n, H, d)
         if ev_before is not None:
             ev_before.record()
-        sdit.attn_fwd(self.q_attn, n, self.segs, self.mask, cfg.block, cfg.block, H, d, self.out, self.lse)
+        if self.kv_parts > 1:
+            for segs, n_segs, mask, o, ls in self.groups:
+                sdit.attn_fwd_partial(self.q_attn, n, segs, mask, cfg.block, cfg.block, H, d, o, ls)
+            if ev_merge is not None:
+                ev_merge.record()
+            sdit.attn_merge([g[3] for g in self.groups], [g[4] for g in self.groups], n, H, d, self.out, self.lse)
+        else:
+            sdit.attn_fwd(self.q_attn, n, self.segs, self.mask, cfg.block, cfg.block, H, d, self.out, self.lse)
         if ev_after is not None:
             ev_after.record()
 
@@ -170,6 +197,8 @@ def main():
     ap.add_argument("--workload", default="wan13b", choices=sorted(W.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--kv-parts", type=int, default=1,
+                    help="split-KV form: attention over this many groups of segments, then the merge")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -197,7 +226,7 @@ def main():
         return
 
     cfg = W.CONFIGS[args.workload]
-    step = Step(cfg, torch, sdit)
+    step = Step(cfg, torch, sdit, args.kv_parts)
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -208,7 +237,8 @@ def main():
     torch.cuda.synchronize()
     h2 = hashlib.md5(step.out.cpu().numpy().tobytes()).hexdigest()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3 if args.kv_parts > 1 else 2))
+           for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -219,7 +249,7 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(end) / args.steps
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
     attn_avg = float(np.mean(attn_ms))
     value = step.flops / (ms_step * 1e-3) / 1e12
     attn_tflops = step.flops / (attn_avg * 1e-3) / 1e12
@@ -253,6 +283,14 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(cfg.name)},
     }
+    if args.kv_parts > 1:
+        merge_ms = float(np.mean([e[2].elapsed_time(e[1]) for e in evs]))
+        gbs = step.merge_bytes / (merge_ms * 1e-3) / 1e9
+        rec["config"]["kv_parts"] = args.kv_parts
+        rec["merge"] = {"kernel": "attn_merge_kernel", "bound": "hbm", "us": round(merge_ms * 1e3, 2),
+                        "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": step.merge_bytes}
+        rec["roofline"]["traffic"] = None
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
     print(json.dumps(rec), flush=True)

@@ -42,6 +42,7 @@ extern "C" {
 
 #define SDIT_ABI_VERSION 1
 #define SDIT_MAX_SEGMENTS 8
+#define SDIT_MAX_MERGE_PARTS 8
 
 typedef enum sdit_status {
   SDIT_OK = 0,
@@ -154,6 +155,41 @@ int sdit_attn_fwd(const void* q, int32_t n_q,
                   int32_t n_heads, int32_t head_dim, float softmax_scale,
                   void* out, float* lse, void* stream);
 
+/* Partial attention for a split of the keys (split-KV): the computation of
+ * sdit_attn_fwd over the given segments, with O written normalised in fp32
+ * so that results over disjoint key sets combine without another rounding
+ * in sdit_attn_merge. Context-parallel attention of the Ulysses / Ring kind
+ * (which the Wave Forcing summary compares Wave Parallelism against) attends
+ * to one key shard per step and merges the shards this way.
+ *   Arguments as sdit_attn_fwd, except
+ *   out   fp32 [n_q][n_heads][head_dim], 16-byte aligned
+ *   lse   fp32 [n_heads][n_q], required (the merge needs it)
+ * A query with no visible key gets o = 0 and lse = -inf. The block mask
+ * covers only the given segments (its columns restart with them). */
+int sdit_attn_fwd_partial(const void* q, int32_t n_q,
+                          const sdit_kv_segment* segs, int32_t n_segs,
+                          const uint8_t* block_mask, int32_t block_q, int32_t block_k,
+                          int32_t n_heads, int32_t head_dim, float softmax_scale,
+                          float* out, float* lse, void* stream);
+
+/* Merge of attention results over disjoint key sets (same passage as
+ * sdit_attn_fwd_partial). Per query and head, with m = max_p lse_p and
+ * w_p = e^(lse_p - m):
+ *   out = sum_p w_p o_p / sum_p w_p   (bf16, rounded once)
+ *   lse_out = m + log sum_p w_p
+ * A part with lse = -inf adds nothing; a query with lse = -inf in every part
+ * gets out = 0 and lse_out = -inf.
+ *   o_parts     HOST array of n_parts device pointers, fp32
+ *               [n_q][n_heads][head_dim], 16-byte aligned
+ *   lse_parts   HOST array of n_parts device pointers, fp32 [n_heads][n_q]
+ *   n_parts     1 .. SDIT_MAX_MERGE_PARTS
+ *   out         bf16 [n_q][n_heads][head_dim]; must not overlap any input
+ *   lse_out     fp32 [n_heads][n_q] or NULL
+ *   head_dim    64 or 128 */
+int sdit_attn_merge(const float* const* o_parts, const float* const* lse_parts, int32_t n_parts,
+                    int32_t n_q, int32_t n_heads, int32_t head_dim,
+                    void* out, float* lse_out, void* stream);
+
 /* Host-only validators: the exact checks the entry points run before a
  * launch, without touching any device. They return SDIT_OK or the status
  * the entry point would return, and set sdit_last_error() likewise. */
@@ -170,6 +206,14 @@ int sdit_validate_attn_args(const void* q, int32_t n_q,
                             const uint8_t* block_mask, int32_t block_q, int32_t block_k,
                             int32_t n_heads, int32_t head_dim, float softmax_scale,
                             const void* out, const float* lse);
+int sdit_validate_attn_partial_args(const void* q, int32_t n_q,
+                                    const sdit_kv_segment* segs, int32_t n_segs,
+                                    const uint8_t* block_mask, int32_t block_q, int32_t block_k,
+                                    int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                    const float* out, const float* lse);
+int sdit_validate_attn_merge_args(const float* const* o_parts, const float* const* lse_parts,
+                                  int32_t n_parts, int32_t n_q, int32_t n_heads, int32_t head_dim,
+                                  const void* out, const float* lse_out);
 
 #ifdef __cplusplus
 }

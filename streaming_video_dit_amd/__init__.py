@@ -53,8 +53,15 @@ def lib() -> ctypes.CDLL:
                                 _vp, _vp, _vp]
     L.sdit_validate_attn_args.argtypes = [_vp, _i32, ctypes.POINTER(KVSegment), _i32, _vp, _i32, _i32, _i32,
                                           _i32, _f32, _vp, _vp]
+    L.sdit_attn_fwd_partial.argtypes = L.sdit_attn_fwd.argtypes
+    L.sdit_validate_attn_partial_args.argtypes = L.sdit_validate_attn_args.argtypes
+    _pp = ctypes.POINTER(ctypes.c_void_p)
+    L.sdit_attn_merge.argtypes = [_pp, _pp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+    L.sdit_validate_attn_merge_args.argtypes = [_pp, _pp, _i32, _i32, _i32, _i32, _vp, _vp]
     for n in ("sdit_qknorm_rope3d", "sdit_validate_qknorm_rope3d_args", "sdit_kv_quant_int8",
-              "sdit_validate_kv_quant_args", "sdit_attn_fwd", "sdit_validate_attn_args"):
+              "sdit_validate_kv_quant_args", "sdit_attn_fwd", "sdit_validate_attn_args",
+              "sdit_attn_fwd_partial", "sdit_validate_attn_partial_args", "sdit_attn_merge",
+              "sdit_validate_attn_merge_args"):
         getattr(L, n).restype = ctypes.c_int
     if L.sdit_abi_version() != ABI_VERSION:
         raise ImportError(f"libsdit.so ABI {L.sdit_abi_version()} != binding ABI {ABI_VERSION}")
@@ -129,6 +136,40 @@ def attn_fwd(q, n_q: int, segs, block_mask, block_q: int, block_k: int, n_heads:
     n = len(segs)
     _check(lib().sdit_attn_fwd(_ptr(q), n_q, arr, n, _ptr(block_mask), block_q, block_k, n_heads, head_dim,
                               softmax_scale, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def attn_fwd_partial(q, n_q: int, segs, block_mask, block_q: int, block_k: int, n_heads: int, head_dim: int,
+                     out, lse, softmax_scale: float = 0.0, stream=None) -> None:
+    """sdit_attn_fwd_partial: ``out`` fp32 [n_q, H, d], ``lse`` fp32 [H, n_q]."""
+    arr = segs if isinstance(segs, ctypes.Array) else make_segments(segs)
+    _check(lib().sdit_attn_fwd_partial(_ptr(q), n_q, arr, len(segs), _ptr(block_mask), block_q, block_k, n_heads,
+                                      head_dim, softmax_scale, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def _pointer_array(xs):
+    arr = (ctypes.c_void_p * max(1, len(xs)))()
+    for i, x in enumerate(xs):
+        arr[i] = _ptr(x)
+    return arr
+
+
+def attn_merge(o_parts, lse_parts, n_q: int, n_heads: int, head_dim: int, out, lse_out=None,
+               stream=None) -> None:
+    """sdit_attn_merge: lists of fp32 partial outputs and their LSEs."""
+    _check(lib().sdit_attn_merge(_pointer_array(o_parts), _pointer_array(lse_parts), len(o_parts), n_q, n_heads,
+                                head_dim, _ptr(out), _ptr(lse_out), _stream(stream)))
+
+
+def validate_attn_partial_args(q, n_q, segs, block_mask, block_q, block_k, n_heads, head_dim, out, lse,
+                               softmax_scale: float = 0.0) -> int:
+    arr = segs if isinstance(segs, ctypes.Array) else make_segments(segs)
+    return lib().sdit_validate_attn_partial_args(_ptr(q), n_q, arr, len(segs), _ptr(block_mask), block_q, block_k,
+                                                n_heads, head_dim, softmax_scale, _ptr(out), _ptr(lse))
+
+
+def validate_attn_merge_args(o_parts, lse_parts, n_q, n_heads, head_dim, out, lse_out=None) -> int:
+    return lib().sdit_validate_attn_merge_args(_pointer_array(o_parts), _pointer_array(lse_parts), len(o_parts),
+                                              n_q, n_heads, head_dim, _ptr(out), _ptr(lse_out))
 
 
 def validate_attn_args(q, n_q, segs, block_mask, block_q, block_k, n_heads, head_dim, out, lse=None,

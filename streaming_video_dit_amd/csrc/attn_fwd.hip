@@ -778,7 +778,17 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   const float l_tot = swap_halves_sum(ws.l_run);
   const bool any = ws.seen && l_tot > 0.f;
   const float inv = any ? 1.0f / l_tot : 0.f;
-  if (q_ok) {
+  if (q_ok && p.out_f32 != nullptr) {
+    // partial form: normalised O in fp32, merged later without another rounding
+    float* op = p.out_f32 + ((int64_t)q_row * p.n_heads + head) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(op + dt * 32 + 8 * g + 4 * hh) =
+            make_float4(any ? ws.o[dt][4 * g + 0] * inv : 0.0f, any ? ws.o[dt][4 * g + 1] * inv : 0.0f,
+                        any ? ws.o[dt][4 * g + 2] * inv : 0.0f, any ? ws.o[dt][4 * g + 3] * inv : 0.0f);
+  } else if (q_ok) {
     uint16_t* op = p.out + ((int64_t)q_row * p.n_heads + head) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -794,6 +804,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
         *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
       }
+  }
+  if (q_ok) {
     if (p.lse != nullptr && hh == 0) {
       const float ln2 = 0.69314718055994530942f;
       p.lse[(int64_t)head * p.n_q + q_row] = any ? (ws.m_run + __log2f(l_tot)) * ln2 : -INFINITY;

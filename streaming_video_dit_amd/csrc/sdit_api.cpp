@@ -166,10 +166,13 @@ SDIT_API int sdit_kv_quant_int8(const void* x, int8_t* codes, float* scales, int
 
 namespace {
 
+// out is bf16 [n_q][H][d], or fp32 when out_f32 (the partial form: lse
+// then required).
 int fill_attn_params(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs,
                      const uint8_t* block_mask, int32_t block_q, int32_t block_k, int32_t n_heads,
                      int32_t head_dim, float softmax_scale, const void* out, const float* lse,
-                     sdit::AttnParams* P) {
+                     sdit::AttnParams* P, bool out_f32 = false) {
+  const char* fn = out_f32 ? "attn_fwd_partial" : "attn_fwd";
   if (head_dim != 64 && head_dim != 128)
     return fail(SDIT_ERR_UNSUPPORTED, "attn_fwd: head_dim %d not in {64, 128}", head_dim);
   if (n_heads < 1) return fail(SDIT_ERR_INVALID, "attn_fwd: n_heads %d < 1", n_heads);
@@ -199,7 +202,7 @@ int fill_attn_params(const void* q, int32_t n_q, const sdit_kv_segment* segs, in
         return fail(SDIT_ERR_INVALID, "attn_fwd: int8 segment %d needs 4-byte aligned k_scale and v_scale", s);
       const int64_t esz = sg.dtype == SDIT_INT8 ? 1 : 2;
       const int64_t seg_bytes = (int64_t)sg.len * n_heads * head_dim * esz;
-      const int64_t out_bytes = (int64_t)n_q * n_heads * head_dim * 2;
+      const int64_t out_bytes = (int64_t)n_q * n_heads * head_dim * (out_f32 ? 4 : 2);
       if (overlap(out, out_bytes, sg.k, seg_bytes) || overlap(out, out_bytes, sg.v, seg_bytes))
         return fail(SDIT_ERR_INVALID, "attn_fwd: out overlaps segment %d", s);
     }
@@ -214,19 +217,22 @@ int fill_attn_params(const void* q, int32_t n_q, const sdit_kv_segment* segs, in
   if (n_q > 0) {
     if (q == nullptr || !aligned(q, 16)) return fail(SDIT_ERR_INVALID, "attn_fwd: q must be non-NULL, 16-byte aligned");
     if (out == nullptr || !aligned(out, 16))
-      return fail(SDIT_ERR_INVALID, "attn_fwd: out must be non-NULL, 16-byte aligned");
-    if (lse != nullptr && !aligned(lse, 4)) return fail(SDIT_ERR_INVALID, "attn_fwd: lse must be 4-byte aligned");
+      return fail(SDIT_ERR_INVALID, "%s: out must be non-NULL, 16-byte aligned", fn);
+    if (out_f32 && lse == nullptr) return fail(SDIT_ERR_INVALID, "%s: lse is required", fn);
+    if (lse != nullptr && !aligned(lse, 4)) return fail(SDIT_ERR_INVALID, "%s: lse must be 4-byte aligned", fn);
     if (kbs > 0 && block_mask == nullptr) return fail(SDIT_ERR_INVALID, "attn_fwd: block_mask is NULL");
     const int64_t qbytes = (int64_t)n_q * n_heads * head_dim * 2;
-    if (overlap(out, qbytes, q, qbytes)) return fail(SDIT_ERR_INVALID, "attn_fwd: out overlaps q");
-    if (lse != nullptr && (overlap(lse, (int64_t)n_q * n_heads * 4, out, qbytes) ||
+    const int64_t obytes = out_f32 ? 2 * qbytes : qbytes;
+    if (overlap(out, obytes, q, qbytes)) return fail(SDIT_ERR_INVALID, "%s: out overlaps q", fn);
+    if (lse != nullptr && (overlap(lse, (int64_t)n_q * n_heads * 4, out, obytes) ||
                            overlap(lse, (int64_t)n_q * n_heads * 4, q, qbytes)))
-      return fail(SDIT_ERR_INVALID, "attn_fwd: lse overlaps q or out");
+      return fail(SDIT_ERR_INVALID, "%s: lse overlaps q or out", fn);
   }
   if (P != nullptr) {
     memset(P, 0, sizeof(*P));
     P->q = (const uint16_t*)q;
-    P->out = (uint16_t*)out;
+    P->out = out_f32 ? nullptr : (uint16_t*)out;
+    P->out_f32 = out_f32 ? (float*)out : nullptr;
     P->lse = (float*)lse;
     P->mask = block_mask;
     int tile = 0, kb = 0;
@@ -264,6 +270,95 @@ SDIT_API int sdit_validate_attn_args(const void* q, int32_t n_q, const sdit_kv_s
                                      int32_t head_dim, float softmax_scale, const void* out, const float* lse) {
   return fill_attn_params(q, n_q, segs, n_segs, block_mask, block_q, block_k, n_heads, head_dim, softmax_scale, out,
                           lse, nullptr);
+}
+
+SDIT_API int sdit_validate_attn_partial_args(const void* q, int32_t n_q, const sdit_kv_segment* segs,
+                                             int32_t n_segs, const uint8_t* block_mask, int32_t block_q,
+                                             int32_t block_k, int32_t n_heads, int32_t head_dim,
+                                             float softmax_scale, const float* out, const float* lse) {
+  return fill_attn_params(q, n_q, segs, n_segs, block_mask, block_q, block_k, n_heads, head_dim, softmax_scale, out,
+                          lse, nullptr, true);
+}
+
+SDIT_API int sdit_attn_fwd_partial(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs,
+                                   const uint8_t* block_mask, int32_t block_q, int32_t block_k, int32_t n_heads,
+                                   int32_t head_dim, float softmax_scale, float* out, float* lse, void* stream) {
+  sdit::AttnParams P;
+  int st = fill_attn_params(q, n_q, segs, n_segs, block_mask, block_q, block_k, n_heads, head_dim, softmax_scale,
+                            out, lse, &P, true);
+  if (st != SDIT_OK) return st;
+  if (n_q == 0) return ok();
+  return device_status(sdit::launch_attn_fwd(P, head_dim, (hipStream_t)stream), "attn_fwd_partial");
+}
+
+// ------------------------------------------------------------------ attn_merge
+
+static_assert(SDIT_MAX_MERGE_PARTS == sdit::kMaxMergeParts, "merge part limit");
+
+namespace {
+
+int fill_merge_params(const float* const* o_parts, const float* const* lse_parts, int32_t n_parts, int32_t n_q,
+                      int32_t n_heads, int32_t head_dim, const void* out, const float* lse_out,
+                      sdit::MergeParams* P) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SDIT_ERR_UNSUPPORTED, "attn_merge: head_dim %d not in {64, 128}", head_dim);
+  if (n_heads < 1) return fail(SDIT_ERR_INVALID, "attn_merge: n_heads %d < 1", n_heads);
+  if (n_q < 0) return fail(SDIT_ERR_INVALID, "attn_merge: n_q %d < 0", n_q);
+  if (n_parts < 1 || n_parts > SDIT_MAX_MERGE_PARTS)
+    return fail(SDIT_ERR_INVALID, "attn_merge: n_parts %d not in [1, %d]", n_parts, SDIT_MAX_MERGE_PARTS);
+  if (o_parts == nullptr || lse_parts == nullptr) return fail(SDIT_ERR_INVALID, "attn_merge: part arrays are NULL");
+  if ((int64_t)n_q * n_heads * head_dim > ((int64_t)1 << 40)) return fail(SDIT_ERR_INVALID, "attn_merge: too large");
+  const int64_t obytes = (int64_t)n_q * n_heads * head_dim * 2;
+  const int64_t fbytes = 2 * obytes, lbytes = (int64_t)n_q * n_heads * 4;
+  if (n_q > 0) {
+    if (out == nullptr || !aligned(out, 16))
+      return fail(SDIT_ERR_INVALID, "attn_merge: out must be non-NULL, 16-byte aligned");
+    if (lse_out != nullptr && !aligned(lse_out, 4))
+      return fail(SDIT_ERR_INVALID, "attn_merge: lse_out must be 4-byte aligned");
+    if (lse_out != nullptr && overlap(lse_out, lbytes, out, obytes))
+      return fail(SDIT_ERR_INVALID, "attn_merge: lse_out overlaps out");
+    for (int i = 0; i < n_parts; ++i) {
+      if (o_parts[i] == nullptr || !aligned(o_parts[i], 16))
+        return fail(SDIT_ERR_INVALID, "attn_merge: part %d output must be non-NULL, 16-byte aligned", i);
+      if (lse_parts[i] == nullptr || !aligned(lse_parts[i], 4))
+        return fail(SDIT_ERR_INVALID, "attn_merge: part %d lse must be non-NULL, 4-byte aligned", i);
+      if (overlap(out, obytes, o_parts[i], fbytes) || overlap(out, obytes, lse_parts[i], lbytes) ||
+          (lse_out != nullptr && (overlap(lse_out, lbytes, o_parts[i], fbytes) ||
+                                  overlap(lse_out, lbytes, lse_parts[i], lbytes))))
+        return fail(SDIT_ERR_INVALID, "attn_merge: outputs overlap part %d", i);
+    }
+  }
+  if (P != nullptr) {
+    memset(P, 0, sizeof(*P));
+    for (int i = 0; i < n_parts; ++i) {
+      P->o[i] = o_parts[i];
+      P->lse[i] = lse_parts[i];
+    }
+    P->n_parts = n_parts;
+    P->n_q = n_q;
+    P->n_heads = n_heads;
+    P->out = (uint16_t*)out;
+    P->lse_out = (float*)lse_out;
+  }
+  return ok();
+}
+
+}  // namespace
+
+SDIT_API int sdit_validate_attn_merge_args(const float* const* o_parts, const float* const* lse_parts,
+                                           int32_t n_parts, int32_t n_q, int32_t n_heads, int32_t head_dim,
+                                           const void* out, const float* lse_out) {
+  return fill_merge_params(o_parts, lse_parts, n_parts, n_q, n_heads, head_dim, out, lse_out, nullptr);
+}
+
+SDIT_API int sdit_attn_merge(const float* const* o_parts, const float* const* lse_parts, int32_t n_parts,
+                             int32_t n_q, int32_t n_heads, int32_t head_dim, void* out, float* lse_out,
+                             void* stream) {
+  sdit::MergeParams P;
+  int st = fill_merge_params(o_parts, lse_parts, n_parts, n_q, n_heads, head_dim, out, lse_out, &P);
+  if (st != SDIT_OK) return st;
+  if (n_q == 0) return ok();
+  return device_status(sdit::launch_attn_merge(P, head_dim, (hipStream_t)stream), "attn_merge");
 }
 
 SDIT_API int sdit_attn_fwd(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs,

@@ -46,7 +46,8 @@ struct AttnSegment {
 
 struct AttnParams {
   const uint16_t* q;
-  uint16_t* out;
+  uint16_t* out;       // bf16 output, or NULL when out_f32 is set
+  float* out_f32;      // partial form: normalised O in fp32
   float* lse;
   const uint8_t* mask;
   AttnSegment seg[kMaxSegments];
@@ -64,5 +65,18 @@ struct AttnParams {
 constexpr int kAttnBQ = 256;  // query rows per workgroup
 constexpr int kAttnBK = 64;   // keys per pipeline stage
 hipError_t launch_attn_fwd(const AttnParams& p, int head_dim, hipStream_t stream);
+
+// ---------------------------------------------------------------- attn_merge
+constexpr int kMaxMergeParts = 8;
+struct MergeParams {
+  const float* o[kMaxMergeParts];    // fp32 [n_q][n_heads][head_dim], normalised
+  const float* lse[kMaxMergeParts];  // fp32 [n_heads][n_q]
+  int32_t n_parts;
+  int32_t n_q;
+  int32_t n_heads;
+  uint16_t* out;                     // bf16 [n_q][n_heads][head_dim]
+  float* lse_out;                    // fp32 [n_heads][n_q] or NULL
+};
+hipError_t launch_attn_merge(const MergeParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace sdit

@@ -113,6 +113,56 @@ def test_attn_validation():
     assert "segment 1" in (v(segs=_segs(s1=dict(dtype=sdit.SDIT_INT8))), sdit.last_error())[1]
 
 
+def test_attn_partial_validation():
+    q, out, mask, lse = A16, A16 + 1000 * MB, A16 + 2000 * MB, A16 + 3000 * MB
+
+    def v(**kw):
+        a = dict(q=q, n_q=300, segs=_segs(), block_mask=mask, block_q=128, block_k=128, n_heads=12, head_dim=128,
+                 out=out, lse=lse)
+        a.update(kw)
+        return sdit.validate_attn_partial_args(**a)
+
+    assert v() == sdit.SDIT_OK
+    assert v(lse=None) == sdit.SDIT_ERR_INVALID                                           # lse required
+    # fp32 output is twice the bf16 size: placed just below q, a bf16 out would end at q, an fp32 one overlaps it
+    q_hi = A16 + 8 * MB
+    assert v(q=q_hi, out=q_hi - 300 * 12 * 128 * 2) == sdit.SDIT_ERR_INVALID
+    assert v(lse=out + 300 * 12 * 128 * 4 - 64) == sdit.SDIT_ERR_INVALID                  # lse overlaps fp32 out
+    assert v(lse=out + 300 * 12 * 128 * 4) == sdit.SDIT_OK
+    assert v(head_dim=96) == sdit.SDIT_ERR_UNSUPPORTED
+    assert v(n_q=0, q=None, out=None, block_mask=None, lse=None) == sdit.SDIT_OK
+    assert "attn_fwd_partial" in (v(lse=None), sdit.last_error())[1]
+
+
+def test_attn_merge_validation():
+    n_q, H, d = 300, 12, 128
+    fbytes, lbytes = n_q * H * d * 4, n_q * H * 4
+    parts = [A16 + i * 64 * MB for i in range(3)]
+    lses = [A16 + 512 * MB + i * MB for i in range(3)]
+    out, lse_out = A16 + 1024 * MB, A16 + 1100 * MB
+
+    def v(**kw):
+        a = dict(o_parts=parts, lse_parts=lses, n_q=n_q, n_heads=H, head_dim=d, out=out, lse_out=lse_out)
+        a.update(kw)
+        return sdit.validate_attn_merge_args(**a)
+
+    assert v() == sdit.SDIT_OK
+    assert v(lse_out=None) == sdit.SDIT_OK
+    assert v(o_parts=[], lse_parts=[]) == sdit.SDIT_ERR_INVALID
+    assert v(o_parts=parts * 3, lse_parts=lses * 3) == sdit.SDIT_ERR_INVALID               # 9 > 8 parts
+    assert v(o_parts=[parts[0]] * 8, lse_parts=[lses[0]] * 8) == sdit.SDIT_OK
+    assert v(o_parts=[parts[0], None, parts[2]]) == sdit.SDIT_ERR_INVALID
+    assert v(o_parts=[parts[0] + 8, parts[1], parts[2]]) == sdit.SDIT_ERR_INVALID         # misaligned
+    assert v(lse_parts=[lses[0], lses[1] + 2, lses[2]]) == sdit.SDIT_ERR_INVALID
+    assert v(out=parts[1] + fbytes - 64) == sdit.SDIT_ERR_INVALID                         # out overlaps a part
+    assert v(lse_out=lses[2] + lbytes - 4) == sdit.SDIT_ERR_INVALID                       # lse_out overlaps
+    assert v(lse_out=out + n_q * H * d * 2 - 4) == sdit.SDIT_ERR_INVALID                  # lse_out overlaps out
+    assert v(head_dim=80) == sdit.SDIT_ERR_UNSUPPORTED
+    assert v(n_heads=0) == sdit.SDIT_ERR_INVALID
+    assert v(n_q=0, out=None) == sdit.SDIT_OK
+    assert "part 1" in (v(o_parts=[parts[0], None, parts[2]]), sdit.last_error())[1]
+
+
 def test_error_message_is_per_call():
     sdit.validate_kv_quant_args(A16, A16 + 8, A16 + 32 * MB, 100, 12, 128)
     assert sdit.last_error() != ""

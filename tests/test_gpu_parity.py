@@ -295,8 +295,9 @@ def test_attention_is_deterministic():
 
 def _sample_rows(n_q, rng, k=24):
     rows = set(range(0, 3)) | set(range(n_q - 3, n_q))
-    last_tile = (n_q - 1) // 128 * 128
-    rows |= {last_tile, min(n_q - 1, last_tile + 1)}
+    for tile in (128, 256):   # first rows of the last half and whole 256-row workgroup tile
+        last_tile = (n_q - 1) // tile * tile
+        rows |= {last_tile, min(n_q - 1, last_tile + 1)}
     rows |= set(rng.choice(n_q, size=k, replace=False).tolist())
     return np.array(sorted(rows))
 
