@@ -304,10 +304,6 @@ __device__ __forceinline__ void issue_part(const AttnParams& p, const TileRef& t
       if (ragged) off = min(tid / L::CPR + jv * RSTEP, t.n_valid - 1) * row_stride + (tid % L::CPR) * 8;
       st.r[jv] = *reinterpret_cast<const uint4*>(vb + off);
     }
-    if (SCALED && j == 0 && tid < BK) {
-      st.ks = p.scale_log2;
-      st.vs = tid < t.n_valid ? 1.0f : 0.0f;
-    }
   } else {
     const int8_t* kb = (const int8_t*)t.k + base;
     const int8_t* vb = (const int8_t*)t.v + base;
@@ -323,12 +319,11 @@ __device__ __forceinline__ void issue_part(const AttnParams& p, const TileRef& t
           st.r[LD::I8CH + ji] = *reinterpret_cast<const uint4*>(vb + off);
       }
     } else if (j == 2 * LD::I8CH && tid < BK) {
-      // keys past the segment end keep a positive K multiplier so their bias stays -1e30
-      const bool ok = tid < t.n_valid;
+      // raw per-key scales; commit_tile turns them into multipliers (using
+      // them here would wait for the loads)
       const int64_t si = (int64_t)(t.key0 + min(tid, t.n_valid - 1)) * p.n_heads + head;
-      const float ksv = t.k_scale[si], vsv = t.v_scale[si];
-      st.ks = ok ? fmaxf(ksv * p.scale_log2, KSC_MIN) : p.scale_log2;
-      st.vs = ok ? vsv : 0.f;
+      st.ks = t.k_scale[si];
+      st.vs = t.v_scale[si];
     }
   }
 }
@@ -343,8 +338,8 @@ __device__ __forceinline__ void issue_tile(const AttnParams& p, const TileRef& t
 // Finish tile t: register-staged V (and int8 K) into LDS buffers vbuf (kbuf),
 // scaled-path multipliers into slot kbuf.
 template <int D, bool SCALED, int LW>
-__device__ __forceinline__ void commit_tile(const TileRef& t, const Stage<D, LW>& st, Smem<D>& sm, int kbuf,
-                                            int vbuf) {
+__device__ __forceinline__ void commit_tile(const AttnParams& p, const TileRef& t, const Stage<D, LW>& st,
+                                            Smem<D>& sm, int kbuf, int vbuf) {
   using L = Layout<D>;
   using LD = Loader<D, LW>;
   const int tid = threadIdx.x;
@@ -370,8 +365,11 @@ __device__ __forceinline__ void commit_tile(const TileRef& t, const Stage<D, LW>
     }
   }
   if (SCALED && tid < BK) {
-    sm.ksc[kbuf][tid] = st.ks;
-    sm.vsc[kbuf][tid] = st.vs;
+    // per-key multipliers of the raw score (log2 units) and of P; keys past the
+    // segment end keep a positive K multiplier so that their bias stays -1e30
+    const bool ok = tid < t.n_valid;
+    sm.ksc[kbuf][tid] = (t.is_int8 && ok) ? fmaxf(st.ks * p.scale_log2, KSC_MIN) : p.scale_log2;
+    sm.vsc[kbuf][tid] = ok ? (t.is_int8 ? st.vs : 1.0f) : 0.0f;
   }
 }
 
@@ -717,7 +715,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     TileRef tn = tile_ref(p, sm.desc[0]);
     if (loader) {
       issue_tile<D, SCALED, LW>(p, tn, head, st, sm, 0, plan);
-      commit_tile<D, SCALED, LW>(tn, st, sm, 0, 0);
+      commit_tile<D, SCALED, LW>(p, tn, st, sm, 0, 0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -763,7 +761,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       } else if (has_next && loader) {
         issue_tile<D, SCALED, LW>(p, tn, head, st, sm, knext, plan);
       }
-      if (has_next && loader) commit_tile<D, SCALED, LW>(tn, st, sm, knext, vnext);
+      if (has_next && loader) commit_tile<D, SCALED, LW>(p, tn, st, sm, knext, vnext);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       vprev = vbuf;
