@@ -212,15 +212,29 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 w) {
 }
 
 // 8 int8 codes (two words) -> 8 bf16 / 8 fp16 (exact: |code| <= 128)
+// Two int8 codes (bytes b, b+1 of w) -> two bf16: |code| <= 128 is exact in
+// fp32 and bf16, so the upper halves of the fp32 values are the bf16 values
+// (one byte permute packs them).
 __device__ __forceinline__ uint32_t i8pair_bf16(uint32_t w, int b) {
-  return (__float_as_uint(i8_at(w, b)) >> 16) | (__float_as_uint(i8_at(w, b + 1)) & 0xFFFF0000u);
+  return __builtin_amdgcn_perm(__float_as_uint(i8_at(w, b + 1)), __float_as_uint(i8_at(w, b)), 0x07060302u);
 }
 __device__ __forceinline__ uint4 i8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return make_uint4(i8pair_bf16(w0, 0), i8pair_bf16(w0, 2), i8pair_bf16(w1, 0), i8pair_bf16(w1, 2));
 }
+// Four int8 codes -> four fp16, exactly: flipping the sign bits gives the
+// bytes u = code + 128 in [0, 255]; placed under the fp16 exponent of 1024
+// (bit pattern 0x6400 | u) they read 1024 + u, and subtracting 1152 leaves
+// the code (an exact difference of nearby values).
+__device__ __forceinline__ uint2 i8x4_to_f16x4(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const f16x2 lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) + bias;
+  const f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) + bias;
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
 __device__ __forceinline__ uint4 i8x8_to_f16x8(uint32_t w0, uint32_t w1) {
-  return make_uint4(pack_f16(i8_at(w0, 0), i8_at(w0, 1)), pack_f16(i8_at(w0, 2), i8_at(w0, 3)),
-                    pack_f16(i8_at(w1, 0), i8_at(w1, 1)), pack_f16(i8_at(w1, 2), i8_at(w1, 3)));
+  const uint2 a = i8x4_to_f16x4(w0), b = i8x4_to_f16x4(w1);
+  return make_uint4(a.x, a.y, b.x, b.y);
 }
 
 // Registers holding the register-staged part of one tile between its global
