@@ -7,11 +7,12 @@
 // d_t, d_h, d_w) are rotated by p_axis * theta^(-2j/d_axis), and the result
 // is rounded to bf16 once.
 //
-// HBM-bound (2 * 2 * d bytes per row and tensor). Work unit: one token, one
-// tensor (q or k) and a group of up to kHeadsPerUnit heads, handled by d/8
-// lanes that each own 8 consecutive columns (16 B per row, coalesced 256 B
-// rows). A lane's four rotation angles depend only on the token, so they are
-// computed once per unit and reused for every head of the unit.
+// HBM-bound (2 * 2 * d bytes per row and tensor). Work unit: one token and a
+// group of up to kHeadsPerUnit heads of both q and k, handled by d/8 lanes
+// that each own 8 consecutive columns (16 B per row, coalesced 256 B rows).
+// A lane's four rotation angles depend only on the token, so they are
+// computed once per unit and reused for the unit's 2 * kHeadsPerUnit rows,
+// whose loads are all issued before the angle math.
 // The arithmetic is fp64 (full rate on CDNA4 vector units, so it costs the
 // same as fp32 here), ending in one correctly rounded fp64 -> bf16
 // conversion. In fp32 a rotation whose two products nearly cancel loses
@@ -50,32 +51,35 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
   const int lane_in_row = threadIdx.x % LPR;
   const int n_hg = (p.n_heads + kHeadsPerUnit - 1) / kHeadsPerUnit;
   const int64_t unit = (int64_t)blockIdx.x * UNITS_PER_BLOCK + threadIdx.x / LPR;
-  const int64_t n_units = (int64_t)p.n_tok * 2 * n_hg;
+  const int64_t n_units = (int64_t)p.n_tok * n_hg;
   const bool active = unit < n_units;
   const int64_t u = active ? unit : 0;
-  const int tok = (int)(u / (2 * n_hg));
-  const int rem = (int)(u % (2 * n_hg));
-  const int is_k = rem / n_hg;
-  const int h0 = (rem % n_hg) * kHeadsPerUnit;
+  const int tok = (int)(u / n_hg);
+  const int h0 = (int)(u % n_hg) * kHeadsPerUnit;
   const int nh = min(kHeadsPerUnit, p.n_heads - h0);
-
-  const uint16_t* in = is_k ? p.k_in : p.q_in;
-  uint16_t* out = is_k ? p.k_out : p.q_out;
-  const float* gamma = is_k ? p.gamma_k : p.gamma_q;
   const int c0 = lane_in_row * 8;
 
-  // Issue the row loads first; they are independent of the angle math.
-  uint4 raw[kHeadsPerUnit];
+  // Issue the row loads first (q rows, then k rows); they are independent of
+  // the angle math.
+  uint4 raw[2 * kHeadsPerUnit];
 #pragma unroll
-  for (int i = 0; i < kHeadsPerUnit; ++i) {
-    if (active && i < nh)
-      raw[i] = *reinterpret_cast<const uint4*>(in + ((int64_t)tok * p.n_heads + h0 + i) * D + c0);
+  for (int i = 0; i < 2 * kHeadsPerUnit; ++i) {
+    const int hi = i % kHeadsPerUnit;
+    const uint16_t* in = i < kHeadsPerUnit ? p.q_in : p.k_in;
+    if (active && hi < nh)
+      raw[i] = *reinterpret_cast<const uint4*>(in + ((int64_t)tok * p.n_heads + h0 + hi) * D + c0);
     else
       raw[i] = make_uint4(0, 0, 0, 0);
   }
-  const float4 g0 = *reinterpret_cast<const float4*>(gamma + c0);
-  const float4 g1 = *reinterpret_cast<const float4*>(gamma + c0 + 4);
-  const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+  float g[2][8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float* gamma = t ? p.gamma_k : p.gamma_q;
+    const float4 g0 = *reinterpret_cast<const float4*>(gamma + c0);
+    const float4 g1 = *reinterpret_cast<const float4*>(gamma + c0 + 4);
+    g[t][0] = g0.x; g[t][1] = g0.y; g[t][2] = g0.z; g[t][3] = g0.w;
+    g[t][4] = g1.x; g[t][5] = g1.y; g[t][6] = g1.z; g[t][7] = g1.w;
+  }
 
   // Token position on the three axes.
   const int HW = p.Hl * p.Wl;
@@ -100,7 +104,8 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
   }
 
 #pragma unroll
-  for (int i = 0; i < kHeadsPerUnit; ++i) {
+  for (int i = 0; i < 2 * kHeadsPerUnit; ++i) {
+    const int t = i / kHeadsPerUnit, hi = i % kHeadsPerUnit;
     double x[8];
     const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
@@ -118,14 +123,15 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
     uint32_t o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const double y0 = x[2 * e] * inv * (double)g[2 * e];
-      const double y1 = x[2 * e + 1] * inv * (double)g[2 * e + 1];
+      const double y0 = x[2 * e] * inv * (double)g[t][2 * e];
+      const double y1 = x[2 * e + 1] * inv * (double)g[t][2 * e + 1];
       const double r0 = y0 * cs[e] - y1 * sn[e];
       const double r1 = y0 * sn[e] + y1 * cs[e];
       o[e] = f64_to_bf16(r0) | (f64_to_bf16(r1) << 16);
     }
-    if (active && i < nh)
-      *reinterpret_cast<uint4*>(out + ((int64_t)tok * p.n_heads + h0 + i) * D + c0) =
+    uint16_t* out = t ? p.k_out : p.q_out;
+    if (active && hi < nh)
+      *reinterpret_cast<uint4*>(out + ((int64_t)tok * p.n_heads + h0 + hi) * D + c0) =
           make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
@@ -134,7 +140,7 @@ template <int D>
 hipError_t launch(const RopeParams& p, hipStream_t stream) {
   constexpr int UNITS_PER_BLOCK = kThreads / (D / 8);
   const int n_hg = (p.n_heads + kHeadsPerUnit - 1) / kHeadsPerUnit;
-  const int64_t n_units = (int64_t)p.n_tok * 2 * n_hg;
+  const int64_t n_units = (int64_t)p.n_tok * n_hg;
   const int64_t blocks = (n_units + UNITS_PER_BLOCK - 1) / UNITS_PER_BLOCK;
   hipLaunchKernelGGL(qknorm_rope3d_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
