@@ -57,8 +57,9 @@ class Step:
         H, d, n = cfg.n_heads, cfg.head_dim, cfg.n_q
         self.q_in, self.k_in, self.v = _dev(inp.q, torch), _dev(inp.k, torch), _dev(inp.v, torch)
         self.gq, self.gk = _dev(inp.gamma_q, torch), _dev(inp.gamma_k, torch)
-        self.q = torch.empty_like(self.q_in)
-        self.k = torch.empty_like(self.k_in)
+        # padding rows between chunks keep their raw values
+        self.q = self.q_in.clone()
+        self.k = self.k_in.clone()
         self.out = torch.empty((n, H, d), dtype=torch.int16, device="cuda")
         self.lse = torch.empty((H, n), dtype=torch.float32, device="cuda")
         self.mask = _dev(inp.mask, torch)
@@ -80,7 +81,9 @@ class Step:
                 self.keep += [kd, vd]
                 segs.append(dict(k=kd, v=vd, len=L, dtype=sdit.SDIT_BF16))
         cur_k = self.k if cfg.rope else self.k_in
-        segs.append(dict(k=cur_k, v=self.v, len=n, dtype=sdit.SDIT_BF16))
+        for c in range(cfg.n_chunks):
+            rows = W.chunk_rows(cfg, c)
+            segs.append(dict(k=cur_k[rows], v=self.v[rows], len=cfg.chunk_tokens, dtype=sdit.SDIT_BF16))
         self.segs = sdit.make_segments(segs)
         self.n_segs = len(segs)
         # split-KV form: groups of consecutive segments, each with its own mask columns
@@ -112,9 +115,11 @@ class Step:
         H, d, n = cfg.n_heads, cfg.head_dim, cfg.n_q
         if cfg.rope:
             dt, dh, dw = cfg.split
-            sdit.qknorm_rope3d(self.q_in, self.k_in, self.q, self.k, self.gq, self.gk, cfg.T, cfg.Hl, cfg.Wl,
-                               cfg.t0, H, d, dt, dh, dw, cfg.theta, cfg.eps)
-        if self.quant_chunk:
+            for c in range(cfg.n_chunks):
+                r = W.chunk_rows(cfg, c)
+                sdit.qknorm_rope3d(self.q_in[r], self.k_in[r], self.q[r], self.k[r], self.gq, self.gk, cfg.T,
+                                   cfg.Hl, cfg.Wl, cfg.t0 + c * cfg.T, H, d, dt, dh, dw, cfg.theta, cfg.eps)
+        if self.quant_chunk:   # single-chunk workloads only
             sdit.kv_quant_int8(self.k, self.ck, self.sk, n, H, d)
             sdit.kv_quant_int8(self.v, self.cv, self.sv, n, H, d)
         if ev_before is not None:
@@ -160,12 +165,14 @@ def cpu_baseline(cfg: W.Config, budget_s: float = 10.0):
         threads = os.cpu_count() or 1
     inp = W.make_inputs(cfg)
     t0 = time.perf_counter()
+    rq, rk = inp.q.copy(), inp.k.copy()
     if cfg.rope:
         dt, dh, dw = cfg.split
-        rq = oracle.qknorm_rope3d(inp.q, inp.gamma_q, cfg.T, cfg.Hl, cfg.Wl, cfg.t0, dt, dh, dw)
-        rk = oracle.qknorm_rope3d(inp.k, inp.gamma_k, cfg.T, cfg.Hl, cfg.Wl, cfg.t0, dt, dh, dw)
-    else:
-        rq, rk = inp.q, inp.k
+        for c in range(cfg.n_chunks):
+            r = W.chunk_rows(cfg, c)
+            t0 = cfg.t0 + c * cfg.T
+            rq[r] = oracle.qknorm_rope3d(inp.q[r], inp.gamma_q, cfg.T, cfg.Hl, cfg.Wl, t0, dt, dh, dw)
+            rk[r] = oracle.qknorm_rope3d(inp.k[r], inp.gamma_k, cfg.T, cfg.Hl, cfg.Wl, t0, dt, dh, dw)
     segs = []
     for i, (k, v) in enumerate(zip(inp.cache_k, inp.cache_v)):
         if cfg.seg_int8[i]:
@@ -174,7 +181,9 @@ def cpu_baseline(cfg: W.Config, budget_s: float = 10.0):
             segs.append({"k": ck, "v": cv, "k_scale": sk, "v_scale": sv, "dtype": "int8"})
         else:
             segs.append({"k": k, "v": v, "dtype": "bf16"})
-    segs.append({"k": rk, "v": inp.v, "dtype": "bf16"})
+    for c in range(cfg.n_chunks):
+        r = W.chunk_rows(cfg, c)
+        segs.append({"k": rk[r], "v": inp.v[r], "dtype": "bf16"})
     heads = 0
     while heads < cfg.n_heads:
         oracle.attention(rq, segs, inp.mask, cfg.block, cfg.block, heads=[heads])

@@ -37,8 +37,8 @@ def ordered(bits: np.ndarray) -> np.ndarray:
 
 
 def segments_for_oracle(inp: W.Inputs, k_cur_bits: np.ndarray, quant=None):
-    """Oracle segment list [cached..., current]. ``quant`` maps a cached
-    segment index to (codes_k, scale_k, codes_v, scale_v)."""
+    """Oracle segment list [cached..., current chunk(s)]. ``quant`` maps a
+    cached segment index to (codes_k, scale_k, codes_v, scale_v)."""
     segs = []
     for i, (k, v) in enumerate(zip(inp.cache_k, inp.cache_v)):
         if quant is not None and i in quant:
@@ -46,7 +46,9 @@ def segments_for_oracle(inp: W.Inputs, k_cur_bits: np.ndarray, quant=None):
             segs.append({"k": ck, "v": cv, "k_scale": sk, "v_scale": sv, "dtype": "int8"})
         else:
             segs.append({"k": k, "v": v, "dtype": "bf16"})
-    segs.append({"k": k_cur_bits, "v": inp.v, "dtype": "bf16"})
+    for c in range(inp.cfg.n_chunks):
+        r = W.chunk_rows(inp.cfg, c)
+        segs.append({"k": k_cur_bits[r], "v": inp.v[r], "dtype": "bf16"})
     return segs
 
 

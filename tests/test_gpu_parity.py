@@ -153,6 +153,26 @@ def test_tiny_workload_end_to_end(name):
     _say(f"   max-abs {e[0]:.2e} ({e[2]:.2e} beyond half an ulp), rel-RMS {e[1]:.2e}")
 
 
+def test_tiny_chunks_end_to_end():
+    """Two query chunks in one forward, RoPE per chunk, chunk-causal mask."""
+    cfg = W.CONFIGS["tiny_chunks"]
+    inp = W.make_inputs(cfg)
+    dt, dh, dw = cfg.split
+    gq, gk, rq, rk = inp.q.copy(), inp.k.copy(), inp.q.copy(), inp.k.copy()
+    for c in range(cfg.n_chunks):
+        r = W.chunk_rows(cfg, c)
+        t0 = cfg.t0 + c * cfg.T
+        gq[r], gk[r] = _gpu_rope((cfg.T, cfg.Hl, cfg.Wl, t0, cfg.split), inp.q[r], inp.k[r], inp.gamma_q,
+                                 inp.gamma_k)
+        rq[r] = oracle.qknorm_rope3d(inp.q[r], inp.gamma_q, cfg.T, cfg.Hl, cfg.Wl, t0, dt, dh, dw)
+        rk[r] = oracle.qknorm_rope3d(inp.k[r], inp.gamma_k, cfg.T, cfg.Hl, cfg.Wl, t0, dt, dh, dw)
+    _say("tiny chunks end to end")
+    out, lse = run_attn(gq, segments_for_oracle(inp, gk), inp.mask, cfg.block, cfg.block)
+    O, LSE = oracle.attention(rq, segments_for_oracle(inp, rk), inp.mask, cfg.block, cfg.block)
+    e = assert_attn_close(out, lse, O, LSE, "tiny_chunks")
+    _say(f"   max-abs {e[0]:.2e} ({e[2]:.2e} beyond half an ulp), rel-RMS {e[1]:.2e}")
+
+
 def test_tiny_mask_readings_differ_on_gpu():
     cfg = W.CONFIGS["tiny"]
     inp = W.make_inputs(cfg)
@@ -302,7 +322,7 @@ def _sample_rows(n_q, rng, k=24):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", ["wan13b", "wan13b_int8", "large_dit", "bsa_sr"])
+@pytest.mark.parametrize("name", ["wan13b", "wan13b_int8", "large_dit", "bsa_sr", "wave_chunks"])
 def test_full_size_hot_path_sampled(name):
     """The benchmark's step at full size: [qknorm_rope3d] -> [kv_quant_int8 of the
     cache] -> attn_fwd on the GPU; the oracle runs the same chain on the CPU and
@@ -313,28 +333,31 @@ def test_full_size_hot_path_sampled(name):
     inp = W.make_inputs(cfg)
     H, d, n_q = cfg.n_heads, cfg.head_dim, cfg.n_q
     _say("full size", name, "n_q", n_q, "keys", sum(cfg.seg_lens))
-    # --- GPU chain
+    # --- GPU chain (RoPE per query chunk; padding rows between chunks stay raw)
+    gq, gk = inp.q.copy(), inp.k.copy()
     if cfg.rope:
-        geo = (cfg.T, cfg.Hl, cfg.Wl, cfg.t0, cfg.split)
-        gq, gk = _gpu_rope(geo, inp.q, inp.k, inp.gamma_q, inp.gamma_k)
-    else:
-        gq, gk = inp.q, inp.k
+        for c in range(cfg.n_chunks):
+            r = W.chunk_rows(cfg, c)
+            geo = (cfg.T, cfg.Hl, cfg.Wl, cfg.t0 + c * cfg.T, cfg.split)
+            gq[r], gk[r] = _gpu_rope(geo, inp.q[r], inp.k[r], inp.gamma_q, inp.gamma_k)
     gpu_quant = {}
-    for i, is8 in enumerate(cfg.seg_int8[:-1]):
+    for i, is8 in enumerate(cfg.seg_int8[:cfg.n_cached]):
         if is8:
             ck, sk = _gpu_quant(inp.cache_k[i])
             cv, sv = _gpu_quant(inp.cache_v[i])
             gpu_quant[i] = (ck, sk, cv, sv)
     out, lse = run_attn(gq, segments_for_oracle(inp, gk, gpu_quant), inp.mask, cfg.block, cfg.block)
     # --- oracle chain
+    rq, rk = inp.q.copy(), inp.k.copy()
     if cfg.rope:
         dt, dh, dw = cfg.split
-        rq = oracle.qknorm_rope3d(inp.q, inp.gamma_q, cfg.T, cfg.Hl, cfg.Wl, cfg.t0, dt, dh, dw)
-        rk = oracle.qknorm_rope3d(inp.k, inp.gamma_k, cfg.T, cfg.Hl, cfg.Wl, cfg.t0, dt, dh, dw)
-    else:
-        rq, rk = inp.q, inp.k
+        for c in range(cfg.n_chunks):
+            r = W.chunk_rows(cfg, c)
+            t0 = cfg.t0 + c * cfg.T
+            rq[r] = oracle.qknorm_rope3d(inp.q[r], inp.gamma_q, cfg.T, cfg.Hl, cfg.Wl, t0, dt, dh, dw)
+            rk[r] = oracle.qknorm_rope3d(inp.k[r], inp.gamma_k, cfg.T, cfg.Hl, cfg.Wl, t0, dt, dh, dw)
     ref_quant = {}
-    for i, is8 in enumerate(cfg.seg_int8[:-1]):
+    for i, is8 in enumerate(cfg.seg_int8[:cfg.n_cached]):
         if is8:
             ck, sk = oracle.kv_quant_int8(inp.cache_k[i])
             cv, sv = oracle.kv_quant_int8(inp.cache_v[i])

@@ -91,11 +91,29 @@ class Config:
     eps: float = 1.0e-6
     bsa_density: float = 0.2
     bsa_frame_tokens: int = 0
+    n_chunks: int = 1      # query chunks in one forward (the last n_chunks segments)
     description: str = ""
 
     @property
-    def n_q(self) -> int:
+    def chunk_tokens(self) -> int:
         return self.T * self.Hl * self.Wl
+
+    @property
+    def chunk_slot(self) -> int:
+        """Query rows per chunk: the chunk's tokens, rounded up to whole
+        blocks when several chunks share one forward (so that no q-block
+        straddles two chunks; the extra rows are padding queries)."""
+        n = self.chunk_tokens
+        return n if self.n_chunks == 1 else -(-n // self.block) * self.block
+
+    @property
+    def n_q(self) -> int:
+        return self.n_chunks * self.chunk_slot
+
+    @property
+    def n_cached(self) -> int:
+        """Number of cached segments (before the chunk segments)."""
+        return len(self.seg_lens) - self.n_chunks
 
     @property
     def split(self):
@@ -131,6 +149,17 @@ CONFIGS: Dict[str, Config] = {
     "bsa_sr": Config("bsa_sr", 12, 128, 8, 66, 66, 0, [34848], [False], 128,
                      "bsa", 4, rope=False, bsa_frame_tokens=66 * 66,
                      description="block-sparse video SR self-attention"),
+    # Staggered chunks in one forward (Wave Forcing summary: block-causal
+    # attention, later chunks read earlier ones): four Wan-1.3B chunks of
+    # 3 x 30 x 52 tokens attend to the text cache, three history chunks and
+    # every chunk up to their own.
+    "wave_chunks": Config("wave_chunks", 12, 128, 3, 30, 52, 9, [512, 14040, 4680, 4680, 4680, 4680],
+                          [False] * 6, 128, "chunk_causal", 5, n_chunks=4,
+                          description="four staggered Wan chunks, chunk-level block-causal mask"),
+    # Tiny version: 2 chunks of 2 x 4 x 5 tokens (40, padded to 48 rows), block 16.
+    "tiny_chunks": Config("tiny_chunks", 2, 64, 2, 4, 5, 2, [16, 80, 40, 40], [False] * 4, 16,
+                          "chunk_causal", 6, n_chunks=2,
+                          description="tiny, two chunks in one forward"),
 }
 
 # Order used by the configs list of the workload definition.
@@ -147,10 +176,19 @@ def make_mask(cfg: Config) -> np.ndarray:
         # Rows are query blocks; a query block sees every cached block and
         # the current-chunk blocks up to and including its own.
         m = np.zeros((nqb, nkb), dtype=np.uint8)
-        n_cache_blocks = sum(-(-L // cfg.block) for L in cfg.seg_lens[:-1])
+        n_cache_blocks = sum(-(-L // cfg.block) for L in cfg.seg_lens[:cfg.n_cached])
         for qb in range(nqb):
             m[qb, :n_cache_blocks] = 1
             m[qb, n_cache_blocks:n_cache_blocks + qb + 1] = 1
+        return m
+    if cfg.mask_kind == "chunk_causal":
+        # q-blocks of chunk c see every cached block and chunks 0..c
+        m = np.zeros((nqb, nkb), dtype=np.uint8)
+        col = np.cumsum([0] + [-(-L // cfg.block) for L in cfg.seg_lens])
+        per_chunk = cfg.chunk_slot // cfg.block
+        for qb in range(nqb):
+            c = qb // per_chunk
+            m[qb, :col[cfg.n_cached + c + 1]] = 1
         return m
     if cfg.mask_kind == "bsa":
         assert len(cfg.seg_lens) == 1
@@ -172,7 +210,7 @@ def make_mask(cfg: Config) -> np.ndarray:
 class Inputs:
     cfg: Config
     q: np.ndarray                  # bf16 bits [n_q, H, d], before norm/rope
-    k: np.ndarray                  # bf16 bits [n_q, H, d], before norm/rope (current chunk)
+    k: np.ndarray                  # bf16 bits [n_q, H, d], before norm/rope (current chunks, see chunk_rows)
     v: np.ndarray                  # bf16 bits [n_q, H, d]
     cache_k: List[np.ndarray] = field(default_factory=list)  # bf16 bits per cached segment
     cache_v: List[np.ndarray] = field(default_factory=list)
@@ -194,7 +232,7 @@ def make_inputs(cfg: Config, n_heads: Optional[int] = None) -> Inputs:
     v = normal_bf16(s, TID_V, (nq, H, d))
     cache_k, cache_v = [], []
     tids = [(TID_TEXT_K, TID_TEXT_V), (TID_HIST_K, TID_HIST_V)]
-    for i, L in enumerate(cfg.seg_lens[:-1]):
+    for i, L in enumerate(cfg.seg_lens[:cfg.n_cached]):
         tk, tv = tids[i]
         p = cfg.outlier_p if cfg.seg_int8[i] else 0.0
         cache_k.append(normal_bf16(s, tk, (L, H, d), p, outlier_tid=TID_K_OUTLIER + 20 * i))
@@ -202,6 +240,12 @@ def make_inputs(cfg: Config, n_heads: Optional[int] = None) -> Inputs:
     gq = uniform_f32(s, TID_GAMMA_Q, (d,), 0.5, 1.5)
     gk = uniform_f32(s, TID_GAMMA_K, (d,), 0.5, 1.5)
     return Inputs(cfg, q, k, v, cache_k, cache_v, gq, gk, make_mask(cfg))
+
+
+def chunk_rows(cfg: Config, c: int) -> slice:
+    """Rows of query chunk c in q / k / v (the rest of its slot is padding)."""
+    start = c * cfg.chunk_slot
+    return slice(start, start + cfg.chunk_tokens)
 
 
 def attn_flops(cfg: Config, mask: np.ndarray) -> int:
