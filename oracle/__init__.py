@@ -24,6 +24,10 @@ What it computes, each function citing the passage it follows:
                       sets by the log-sum-exp identity (the shard merge of
                       Ulysses / Ring context parallelism, which the Wave
                       Forcing summary compares against).
+  * ``window``        window-major token order of windowed sparse attention
+                      and its locality mask (FlashVSR deployment notes,
+                      spatial tiling section: 8 x 8-token attention blocks,
+                      local_range in blocks).
 
 Readings of points the pages leave open are stated in each function.
 Parity pinning: every function is pinned by the ``-m "not gpu"`` tests in
@@ -37,10 +41,12 @@ from .bf16 import bf16_to_f64, f64_to_bf16
 from .qknorm_rope3d import rms_norm, rope3d_angles, apply_rope, qknorm_rope3d
 from .kv_quant import kv_quant_int8, kv_dequant
 from .attention import key_block_index, attention, segment_values, attention_merge
+from .window import window_order, window_coords, local_window_mask
 
 __all__ = [
     "bf16_to_f64", "f64_to_bf16",
     "rms_norm", "rope3d_angles", "apply_rope", "qknorm_rope3d",
     "kv_quant_int8", "kv_dequant",
     "key_block_index", "attention", "segment_values", "attention_merge",
+    "window_order", "window_coords", "local_window_mask",
 ]
