@@ -80,10 +80,15 @@ class Step:
             else:
                 self.keep += [kd, vd]
                 segs.append(dict(k=kd, v=vd, len=L, dtype=sdit.SDIT_BF16))
-        cur_k = self.k if cfg.rope else self.k_in
+        cur_k, cur_v = (self.k if cfg.rope else self.k_in), self.v
+        if cfg.window:
+            # windowed attention runs on window-major copies; the output is put back in raster order
+            self.q_w, self.k_w, self.v_w = (torch.empty_like(self.q_in) for _ in range(3))
+            self.out_w = torch.empty_like(self.out)
+            cur_k, cur_v = self.k_w, self.v_w
         for c in range(cfg.n_chunks):
             rows = W.chunk_rows(cfg, c)
-            segs.append(dict(k=cur_k[rows], v=self.v[rows], len=cfg.chunk_tokens, dtype=sdit.SDIT_BF16))
+            segs.append(dict(k=cur_k[rows], v=cur_v[rows], len=cfg.chunk_tokens, dtype=sdit.SDIT_BF16))
         self.segs = sdit.make_segments(segs)
         self.n_segs = len(segs)
         # split-KV form: groups of consecutive segments, each with its own mask columns
@@ -100,7 +105,7 @@ class Step:
                 ls = torch.empty((H, n), dtype=torch.float32, device="cuda")
                 self.groups.append((sdit.make_segments(segs[a:b]), b - a, _dev(cols, torch), o, ls))
             self.merge_bytes = (kv_parts * (4 * d + 4) + 2 * d + 4) * n * H
-        self.q_attn = self.q if cfg.rope else self.q_in
+        self.q_attn = self.q_w if cfg.window else (self.q if cfg.rope else self.q_in)
         self.quant_chunk = any(cfg.seg_int8)
         if self.quant_chunk:
             self.ck = torch.empty((n, H, d), dtype=torch.int8, device="cuda")
@@ -122,6 +127,10 @@ class Step:
         if self.quant_chunk:   # single-chunk workloads only
             sdit.kv_quant_int8(self.k, self.ck, self.sk, n, H, d)
             sdit.kv_quant_int8(self.v, self.cv, self.sv, n, H, d)
+        if cfg.window:
+            for src, dst in ((self.q_in, self.q_w), (self.k_in, self.k_w), (self.v, self.v_w)):
+                sdit.window_permute(src, dst, cfg.T, cfg.Hl, cfg.Wl, H, d, cfg.window)
+        out = self.out_w if cfg.window else self.out
         if ev_before is not None:
             ev_before.record()
         if self.kv_parts > 1:
@@ -129,11 +138,13 @@ class Step:
                 sdit.attn_fwd_partial(self.q_attn, n, segs, mask, cfg.block, cfg.block, H, d, o, ls)
             if ev_merge is not None:
                 ev_merge.record()
-            sdit.attn_merge([g[3] for g in self.groups], [g[4] for g in self.groups], n, H, d, self.out, self.lse)
+            sdit.attn_merge([g[3] for g in self.groups], [g[4] for g in self.groups], n, H, d, out, self.lse)
         else:
-            sdit.attn_fwd(self.q_attn, n, self.segs, self.mask, cfg.block, cfg.block, H, d, self.out, self.lse)
+            sdit.attn_fwd(self.q_attn, n, self.segs, self.mask, cfg.block, cfg.block, H, d, out, self.lse)
         if ev_after is not None:
             ev_after.record()
+        if cfg.window:
+            sdit.window_permute(self.out_w, self.out, cfg.T, cfg.Hl, cfg.Wl, H, d, cfg.window, inverse=True)
 
 
 def measured_traffic(workload: str):
@@ -181,9 +192,13 @@ def cpu_baseline(cfg: W.Config, budget_s: float = 10.0):
             segs.append({"k": ck, "v": cv, "k_scale": sk, "v_scale": sv, "dtype": "int8"})
         else:
             segs.append({"k": k, "v": v, "dtype": "bf16"})
+    v = inp.v
+    if cfg.window:
+        order = oracle.window_order(cfg.T, cfg.Hl, cfg.Wl, cfg.window)
+        rq, rk, v = rq[order], rk[order], v[order]
     for c in range(cfg.n_chunks):
         r = W.chunk_rows(cfg, c)
-        segs.append({"k": rk[r], "v": inp.v[r], "dtype": "bf16"})
+        segs.append({"k": rk[r], "v": v[r], "dtype": "bf16"})
     heads = 0
     while heads < cfg.n_heads:
         oracle.attention(rq, segs, inp.mask, cfg.block, cfg.block, heads=[heads])

@@ -190,6 +190,20 @@ int sdit_attn_merge(const float* const* o_parts, const float* const* lse_parts, 
                     int32_t n_q, int32_t n_heads, int32_t head_dim,
                     void* out, float* lse_out, void* stream);
 
+/* Token reordering for windowed sparse attention (FlashVSR deployment
+ * notes, spatial tiling section: one attention block is a window of 8 x 8
+ * tokens, and local_range counts such blocks). Tokens of a clip of T frames
+ * of Hl x Wl tokens move between raster order (t, h, w) and window-major
+ * order (t, h / window, w / window, h % window, w % window), so that every
+ * window x window consecutive tokens form one spatial window (a block of
+ * sdit_attn_fwd with block size window^2).
+ *   x, y       bf16 [T*Hl*Wl][n_heads][head_dim]; must not overlap
+ *   inverse    0: x raster -> y window-major; 1: x window-major -> y raster
+ *   window     2, 4, 8 or 16; Hl and Wl multiples of it
+ *   head_dim   64 or 128; T, Hl or Wl == 0 is a no-op. */
+int sdit_window_permute(const void* x, void* y, int32_t T, int32_t Hl, int32_t Wl,
+                        int32_t n_heads, int32_t head_dim, int32_t window, int32_t inverse, void* stream);
+
 /* Host-only validators: the exact checks the entry points run before a
  * launch, without touching any device. They return SDIT_OK or the status
  * the entry point would return, and set sdit_last_error() likewise. */
@@ -211,6 +225,8 @@ int sdit_validate_attn_partial_args(const void* q, int32_t n_q,
                                     const uint8_t* block_mask, int32_t block_q, int32_t block_k,
                                     int32_t n_heads, int32_t head_dim, float softmax_scale,
                                     const float* out, const float* lse);
+int sdit_validate_window_permute_args(const void* x, const void* y, int32_t T, int32_t Hl, int32_t Wl,
+                                      int32_t n_heads, int32_t head_dim, int32_t window, int32_t inverse);
 int sdit_validate_attn_merge_args(const float* const* o_parts, const float* const* lse_parts,
                                   int32_t n_parts, int32_t n_q, int32_t n_heads, int32_t head_dim,
                                   const void* out, const float* lse_out);

@@ -58,7 +58,10 @@ def lib() -> ctypes.CDLL:
     _pp = ctypes.POINTER(ctypes.c_void_p)
     L.sdit_attn_merge.argtypes = [_pp, _pp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
     L.sdit_validate_attn_merge_args.argtypes = [_pp, _pp, _i32, _i32, _i32, _i32, _vp, _vp]
-    for n in ("sdit_qknorm_rope3d", "sdit_validate_qknorm_rope3d_args", "sdit_kv_quant_int8",
+    L.sdit_window_permute.argtypes = [_vp, _vp] + [_i32] * 7 + [_vp]
+    L.sdit_validate_window_permute_args.argtypes = [_vp, _vp] + [_i32] * 7
+    for n in ("sdit_window_permute", "sdit_validate_window_permute_args",
+              "sdit_qknorm_rope3d", "sdit_validate_qknorm_rope3d_args", "sdit_kv_quant_int8",
               "sdit_validate_kv_quant_args", "sdit_attn_fwd", "sdit_validate_attn_args",
               "sdit_attn_fwd_partial", "sdit_validate_attn_partial_args", "sdit_attn_merge",
               "sdit_validate_attn_merge_args"):
@@ -112,6 +115,18 @@ def qknorm_rope3d(q_in, k_in, q_out, k_out, gamma_q, gamma_k, T: int, Hl: int, W
 def kv_quant_int8(x, codes, scales, n_tok: int, n_heads: int, head_dim: int, stream=None) -> None:
     """sdit_kv_quant_int8."""
     _check(lib().sdit_kv_quant_int8(_ptr(x), _ptr(codes), _ptr(scales), n_tok, n_heads, head_dim, _stream(stream)))
+
+
+def window_permute(x, y, T: int, Hl: int, Wl: int, n_heads: int, head_dim: int, window: int = 8,
+                   inverse: bool = False, stream=None) -> None:
+    """sdit_window_permute."""
+    _check(lib().sdit_window_permute(_ptr(x), _ptr(y), T, Hl, Wl, n_heads, head_dim, window, int(inverse),
+                                    _stream(stream)))
+
+
+def validate_window_permute_args(x, y, T, Hl, Wl, n_heads, head_dim, window=8, inverse=False) -> int:
+    return lib().sdit_validate_window_permute_args(_ptr(x), _ptr(y), T, Hl, Wl, n_heads, head_dim, window,
+                                                  int(inverse))
 
 
 def make_segments(segs: Sequence[dict]):

@@ -361,6 +361,60 @@ SDIT_API int sdit_attn_merge(const float* const* o_parts, const float* const* ls
   return device_status(sdit::launch_attn_merge(P, head_dim, (hipStream_t)stream), "attn_merge");
 }
 
+// ------------------------------------------------------------------ window_permute
+
+namespace {
+
+int fill_permute_params(const void* x, const void* y, int32_t T, int32_t Hl, int32_t Wl, int32_t n_heads,
+                        int32_t head_dim, int32_t window, int32_t inverse, sdit::PermuteParams* P) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SDIT_ERR_UNSUPPORTED, "window_permute: head_dim %d not in {64, 128}", head_dim);
+  if (window != 2 && window != 4 && window != 8 && window != 16)
+    return fail(SDIT_ERR_UNSUPPORTED, "window_permute: window %d not in {2, 4, 8, 16}", window);
+  if (T < 0 || Hl < 0 || Wl < 0 || n_heads < 1)
+    return fail(SDIT_ERR_INVALID, "window_permute: bad shape T=%d Hl=%d Wl=%d n_heads=%d", T, Hl, Wl, n_heads);
+  if (Hl % window != 0 || Wl % window != 0)
+    return fail(SDIT_ERR_INVALID, "window_permute: frame %d x %d is not whole %d x %d windows", Hl, Wl, window,
+                window);
+  if (inverse != 0 && inverse != 1) return fail(SDIT_ERR_INVALID, "window_permute: inverse must be 0 or 1");
+  const int64_t n_tok = (int64_t)T * Hl * Wl;
+  if (n_tok > INT32_MAX / 2) return fail(SDIT_ERR_INVALID, "window_permute: too many tokens");
+  const int64_t bytes = n_tok * n_heads * head_dim * 2;
+  if (n_tok > 0) {
+    if (x == nullptr || y == nullptr || !aligned(x, 16) || !aligned(y, 16))
+      return fail(SDIT_ERR_INVALID, "window_permute: x and y must be non-NULL, 16-byte aligned");
+    if (overlap(x, bytes, y, bytes)) return fail(SDIT_ERR_INVALID, "window_permute: x and y overlap");
+  }
+  if (P != nullptr) {
+    P->x = (const uint16_t*)x;
+    P->y = (uint16_t*)y;
+    P->T = T;
+    P->Hl = Hl;
+    P->Wl = Wl;
+    P->win = window;
+    P->row_chunks = n_heads * head_dim / 8;
+    P->inverse = inverse;
+    P->n_tok = n_tok;
+  }
+  return ok();
+}
+
+}  // namespace
+
+SDIT_API int sdit_validate_window_permute_args(const void* x, const void* y, int32_t T, int32_t Hl, int32_t Wl,
+                                               int32_t n_heads, int32_t head_dim, int32_t window, int32_t inverse) {
+  return fill_permute_params(x, y, T, Hl, Wl, n_heads, head_dim, window, inverse, nullptr);
+}
+
+SDIT_API int sdit_window_permute(const void* x, void* y, int32_t T, int32_t Hl, int32_t Wl, int32_t n_heads,
+                                 int32_t head_dim, int32_t window, int32_t inverse, void* stream) {
+  sdit::PermuteParams P;
+  int st = fill_permute_params(x, y, T, Hl, Wl, n_heads, head_dim, window, inverse, &P);
+  if (st != SDIT_OK) return st;
+  if (P.n_tok == 0) return ok();
+  return device_status(sdit::launch_window_permute(P, (hipStream_t)stream), "window_permute");
+}
+
 SDIT_API int sdit_attn_fwd(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs,
                            const uint8_t* block_mask, int32_t block_q, int32_t block_k, int32_t n_heads,
                            int32_t head_dim, float softmax_scale, void* out, float* lse, void* stream) {

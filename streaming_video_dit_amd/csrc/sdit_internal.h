@@ -79,4 +79,15 @@ struct MergeParams {
 };
 hipError_t launch_attn_merge(const MergeParams& p, int head_dim, hipStream_t stream);
 
+// ---------------------------------------------------------------- window_permute
+struct PermuteParams {
+  const uint16_t* x;
+  uint16_t* y;
+  int32_t T, Hl, Wl, win;
+  int32_t row_chunks;   // 16-byte chunks per token row (n_heads * head_dim / 8)
+  int32_t inverse;      // 0: raster -> window-major, 1: window-major -> raster
+  int64_t n_tok;
+};
+hipError_t launch_window_permute(const PermuteParams& p, hipStream_t stream);
+
 }  // namespace sdit

@@ -163,6 +163,26 @@ def test_attn_merge_validation():
     assert "part 1" in (v(o_parts=[parts[0], None, parts[2]]), sdit.last_error())[1]
 
 
+def test_window_permute_validation():
+    x, y = A16, A16 + 256 * MB            # 2 x 96 x 168 tokens x 12 heads x 128 bf16 = 99 MB each
+
+    def v(**kw):
+        a = dict(x=x, y=y, T=2, Hl=96, Wl=168, n_heads=12, head_dim=128, window=8, inverse=False)
+        a.update(kw)
+        return sdit.validate_window_permute_args(**a)
+
+    assert v() == sdit.SDIT_OK
+    assert v(inverse=True) == sdit.SDIT_OK
+    assert v(Wl=164) == sdit.SDIT_ERR_INVALID            # not whole windows
+    assert v(window=6) == sdit.SDIT_ERR_UNSUPPORTED
+    assert v(head_dim=96) == sdit.SDIT_ERR_UNSUPPORTED
+    assert v(y=x + 1024) == sdit.SDIT_ERR_INVALID         # overlap (no in-place reordering)
+    assert v(y=y + 8) == sdit.SDIT_ERR_INVALID            # misaligned
+    assert v(x=None) == sdit.SDIT_ERR_INVALID
+    assert v(T=0, x=None, y=None) == sdit.SDIT_OK
+    assert v(n_heads=0) == sdit.SDIT_ERR_INVALID
+
+
 def test_error_message_is_per_call():
     sdit.validate_kv_quant_args(A16, A16 + 8, A16 + 32 * MB, 100, 12, 128)
     assert sdit.last_error() != ""

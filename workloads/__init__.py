@@ -92,6 +92,8 @@ class Config:
     bsa_density: float = 0.2
     bsa_frame_tokens: int = 0
     n_chunks: int = 1      # query chunks in one forward (the last n_chunks segments)
+    window: int = 0        # > 0: windowed attention, tokens reordered window by window (block = window^2)
+    local_range: int = 0   # windows kept around a query window (mask kind "local")
     description: str = ""
 
     @property
@@ -156,6 +158,16 @@ CONFIGS: Dict[str, Config] = {
     "wave_chunks": Config("wave_chunks", 12, 128, 3, 30, 52, 9, [512, 14040, 4680, 4680, 4680, 4680],
                           [False] * 6, 128, "chunk_causal", 5, n_chunks=4,
                           description="four staggered Wan chunks, chunk-level block-causal mask"),
+    # Windowed locality-sparse SR self-attention (FlashVSR deployment notes,
+    # spatial tiling section): the page's 2688 x 1536 clip is 168 x 96 tokens
+    # per frame, attention blocks are 8 x 8-token windows (64 tokens), and
+    # local_range = 11 windows; two latent frames.
+    "vsr_local": Config("vsr_local", 12, 128, 2, 96, 168, 0, [2 * 96 * 168], [False], 64, "local", 7,
+                        rope=False, window=8, local_range=11,
+                        description="windowed locality-sparse SR self-attention, 2 frames of 96 x 168 tokens"),
+    "tiny_local": Config("tiny_local", 2, 64, 2, 16, 24, 0, [2 * 16 * 24], [False], 16, "local", 8,
+                         rope=False, window=4, local_range=3,
+                         description="tiny windowed locality-sparse self-attention"),
     # Tiny version: 2 chunks of 2 x 4 x 5 tokens (40, padded to 48 rows), block 16.
     "tiny_chunks": Config("tiny_chunks", 2, 64, 2, 4, 5, 2, [16, 80, 40, 40], [False] * 4, 16,
                           "chunk_causal", 6, n_chunks=2,
@@ -181,6 +193,16 @@ def make_mask(cfg: Config) -> np.ndarray:
             m[qb, :n_cache_blocks] = 1
             m[qb, n_cache_blocks:n_cache_blocks + qb + 1] = 1
         return m
+    if cfg.mask_kind == "local":
+        # blocks are windows in window-major order (frame, window row, window
+        # column); a key window is kept when it lies within local_range // 2
+        # windows of the query window in both directions, in any frame
+        assert cfg.block == cfg.window * cfg.window and nqb == nkb
+        nwy, nwx = cfg.Hl // cfg.window, cfg.Wl // cfg.window
+        b = np.arange(nqb) % (nwy * nwx)
+        wy, wx = b // nwx, b % nwx
+        r = cfg.local_range // 2
+        return ((np.abs(wy[:, None] - wy[None, :]) <= r) & (np.abs(wx[:, None] - wx[None, :]) <= r)).astype(np.uint8)
     if cfg.mask_kind == "chunk_causal":
         # q-blocks of chunk c see every cached block and chunks 0..c
         m = np.zeros((nqb, nkb), dtype=np.uint8)
