@@ -24,6 +24,9 @@ What it computes, each function citing the passage it follows:
                       sets by the log-sum-exp identity (the shard merge of
                       Ulysses / Ring context parallelism, which the Wave
                       Forcing summary compares against).
+  * ``norms``         RMSNorm and LayerNorm + modulate over the hidden
+                      dimension (the other fused kernels the same README
+                      lists, table of changed files).
   * ``window``        window-major token order of windowed sparse attention
                       and its locality mask (FlashVSR deployment notes,
                       spatial tiling section: 8 x 8-token attention blocks,
@@ -42,6 +45,7 @@ from .qknorm_rope3d import rms_norm, rope3d_angles, apply_rope, qknorm_rope3d
 from .kv_quant import kv_quant_int8, kv_dequant
 from .attention import key_block_index, attention, segment_values, attention_merge
 from .window import window_order, window_coords, local_window_mask
+from .norms import rmsnorm, layernorm_modulate
 
 __all__ = [
     "bf16_to_f64", "f64_to_bf16",
@@ -49,4 +53,5 @@ __all__ = [
     "kv_quant_int8", "kv_dequant",
     "key_block_index", "attention", "segment_values", "attention_merge",
     "window_order", "window_coords", "local_window_mask",
+    "rmsnorm", "layernorm_modulate",
 ]
