@@ -12,6 +12,12 @@ segments are cut into N groups of consecutive segments, attn_fwd_partial
 runs once per group (fp32 partial O and LSE) and attn_merge combines them;
 the line then also reports the merge kernel against the HBM roofline.
 
+With --with-norms the line also carries a "norms" object: RMSNorm and
+LayerNorm + modulate over the hidden state of the workload's query tokens
+(n_q x n_heads*head_dim bf16), each timed alone after the attention steps
+against the HBM roofline. They are not part of the step and do not change
+``value``.
+
 Prints ONE JSON line. ``value`` is effective attention TFLOP/s of the whole
 step (kept-tile FLOPs 4*d*H*sum rows*cols / step time); ``ms_per_step`` is
 the ms/layer/chunk. ``roofline`` reports the attention kernel alone, timed
@@ -147,6 +153,38 @@ class Step:
             sdit.window_permute(self.out_w, self.out, cfg.T, cfg.Hl, cfg.Wl, H, d, cfg.window, inverse=True)
 
 
+def measure_norms(cfg: W.Config, torch, sdit, steps: int, warmup: int):
+    """Average launch time and HBM rate of the two per-token norms on the
+    workload's hidden-state shape (algorithmic bytes: x read and y written
+    once, 2 + 2 bytes per element, plus the fp32 parameter vectors once)."""
+    n, d = cfg.n_q, cfg.n_heads * cfg.head_dim
+    inp = W.make_norm_inputs(cfg.seed, n, d, offset=1.0)
+    x = _dev(inp.x, torch)
+    y = torch.empty_like(x)
+    g, sc, sh = _dev(inp.gamma, torch), _dev(inp.scale, torch), _dev(inp.shift, torch)
+    launches = {
+        "rmsnorm": (lambda: sdit.rmsnorm(x, y, g, n, d), 4 * n * d + 4 * d),
+        "layernorm_modulate": (lambda: sdit.layernorm_modulate(x, y, sc, sh, n, d), 4 * n * d + 8 * d),
+    }
+    res = {"shape": [n, d]}
+    stream = torch.cuda.current_stream()
+    for name, (fn, nbytes) in launches.items():
+        for _ in range(warmup):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"kernel": f"norm_kernel<{(d // 8 + 63) // 64}, {'true' if name != 'rmsnorm' else 'false'}>",
+                     "bound": "hbm", "us": round(us, 2), "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes}
+    return res
+
+
 def measured_traffic(workload: str):
     """HBM bytes per attention launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE
     runs summarised under profiles/ (calibrated against a plain copy). The
@@ -223,6 +261,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--kv-parts", type=int, default=1,
                     help="split-KV form: attention over this many groups of segments, then the merge")
+    ap.add_argument("--with-norms", action="store_true",
+                    help="also time RMSNorm and LayerNorm + modulate on the workload's hidden-state shape")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -315,6 +355,8 @@ def main():
                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": step.merge_bytes}
         rec["roofline"]["traffic"] = None
+    if args.with_norms:
+        rec["norms"] = measure_norms(cfg, torch, sdit, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
     print(json.dumps(rec), flush=True)

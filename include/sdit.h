@@ -204,6 +204,27 @@ int sdit_attn_merge(const float* const* o_parts, const float* const* lse_parts, 
 int sdit_window_permute(const void* x, void* y, int32_t T, int32_t Hl, int32_t Wl,
                         int32_t n_heads, int32_t head_dim, int32_t window, int32_t inverse, void* stream);
 
+/* Per-token normalisations of the DiT block over the hidden dimension
+ * (Joy-face_change_optimized README, table of changed files: RMSNorm and
+ * LayerNorm + modulate are fused kernels beside QK-norm + 3D RoPE; the pages
+ * give no formulas, so these are the usual definitions). Arithmetic in fp64,
+ * one rounding to bf16 per output.
+ *   sdit_rmsnorm:            y = x / sqrt(mean(x^2) + eps) * gamma
+ *   sdit_layernorm_modulate: y = (x - mean) / sqrt(var + eps) * (1 + scale) + shift
+ *                            (population variance; no affine parameters of its own)
+ *   x, y          bf16 [n_tok][dim]; y == x (in place) is allowed, any other
+ *                 overlap is rejected; 16-byte aligned
+ *   gamma, scale, shift  fp32 [dim], shared by every token; 16-byte aligned
+ *   dim           multiple of 8, 8 .. SDIT_MAX_NORM_DIM
+ *   n_tok         0 .. 2^26 - 1; 0 is a no-op
+ *   eps           0 <= eps <= 1
+ * The library keeps no pointer past the call; nothing is allocated. */
+#define SDIT_MAX_NORM_DIM 8192
+int sdit_rmsnorm(const void* x, void* y, const float* gamma, int64_t n_tok, int32_t dim, float eps,
+                 void* stream);
+int sdit_layernorm_modulate(const void* x, void* y, const float* scale, const float* shift,
+                            int64_t n_tok, int32_t dim, float eps, void* stream);
+
 /* Host-only validators: the exact checks the entry points run before a
  * launch, without touching any device. They return SDIT_OK or the status
  * the entry point would return, and set sdit_last_error() likewise. */
@@ -230,6 +251,10 @@ int sdit_validate_window_permute_args(const void* x, const void* y, int32_t T, i
 int sdit_validate_attn_merge_args(const float* const* o_parts, const float* const* lse_parts,
                                   int32_t n_parts, int32_t n_q, int32_t n_heads, int32_t head_dim,
                                   const void* out, const float* lse_out);
+int sdit_validate_rmsnorm_args(const void* x, const void* y, const float* gamma, int64_t n_tok,
+                               int32_t dim, float eps);
+int sdit_validate_layernorm_modulate_args(const void* x, const void* y, const float* scale,
+                                          const float* shift, int64_t n_tok, int32_t dim, float eps);
 
 #ifdef __cplusplus
 }

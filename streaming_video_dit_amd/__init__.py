@@ -60,7 +60,13 @@ def lib() -> ctypes.CDLL:
     L.sdit_validate_attn_merge_args.argtypes = [_pp, _pp, _i32, _i32, _i32, _i32, _vp, _vp]
     L.sdit_window_permute.argtypes = [_vp, _vp] + [_i32] * 7 + [_vp]
     L.sdit_validate_window_permute_args.argtypes = [_vp, _vp] + [_i32] * 7
-    for n in ("sdit_window_permute", "sdit_validate_window_permute_args",
+    _i64 = ctypes.c_int64
+    L.sdit_rmsnorm.argtypes = [_vp, _vp, _vp, _i64, _i32, _f32, _vp]
+    L.sdit_validate_rmsnorm_args.argtypes = [_vp, _vp, _vp, _i64, _i32, _f32]
+    L.sdit_layernorm_modulate.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _f32, _vp]
+    L.sdit_validate_layernorm_modulate_args.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _f32]
+    for n in ("sdit_window_permute", "sdit_validate_window_permute_args", "sdit_rmsnorm",
+              "sdit_validate_rmsnorm_args", "sdit_layernorm_modulate", "sdit_validate_layernorm_modulate_args",
               "sdit_qknorm_rope3d", "sdit_validate_qknorm_rope3d_args", "sdit_kv_quant_int8",
               "sdit_validate_kv_quant_args", "sdit_attn_fwd", "sdit_validate_attn_args",
               "sdit_attn_fwd_partial", "sdit_validate_attn_partial_args", "sdit_attn_merge",
@@ -127,6 +133,26 @@ def window_permute(x, y, T: int, Hl: int, Wl: int, n_heads: int, head_dim: int, 
 def validate_window_permute_args(x, y, T, Hl, Wl, n_heads, head_dim, window=8, inverse=False) -> int:
     return lib().sdit_validate_window_permute_args(_ptr(x), _ptr(y), T, Hl, Wl, n_heads, head_dim, window,
                                                   int(inverse))
+
+
+def rmsnorm(x, y, gamma, n_tok: int, dim: int, eps: float = 1e-6, stream=None) -> None:
+    """sdit_rmsnorm."""
+    _check(lib().sdit_rmsnorm(_ptr(x), _ptr(y), _ptr(gamma), n_tok, dim, eps, _stream(stream)))
+
+
+def validate_rmsnorm_args(x, y, gamma, n_tok, dim, eps=1e-6) -> int:
+    return lib().sdit_validate_rmsnorm_args(_ptr(x), _ptr(y), _ptr(gamma), n_tok, dim, eps)
+
+
+def layernorm_modulate(x, y, scale, shift, n_tok: int, dim: int, eps: float = 1e-6, stream=None) -> None:
+    """sdit_layernorm_modulate."""
+    _check(lib().sdit_layernorm_modulate(_ptr(x), _ptr(y), _ptr(scale), _ptr(shift), n_tok, dim, eps,
+                                         _stream(stream)))
+
+
+def validate_layernorm_modulate_args(x, y, scale, shift, n_tok, dim, eps=1e-6) -> int:
+    return lib().sdit_validate_layernorm_modulate_args(_ptr(x), _ptr(y), _ptr(scale), _ptr(shift), n_tok, dim,
+                                                       eps)
 
 
 def make_segments(segs: Sequence[dict]):

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsdit.so")
 
-SOURCES = ["sdit_api.cpp", "qknorm_rope3d.hip", "kv_quant_int8.hip", "attn_fwd.hip", "attn_merge.hip", "window_permute.hip"]
+SOURCES = ["sdit_api.cpp", "qknorm_rope3d.hip", "kv_quant_int8.hip", "attn_fwd.hip", "attn_merge.hip", "window_permute.hip",
+           "norms.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",

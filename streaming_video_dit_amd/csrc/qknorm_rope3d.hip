@@ -29,21 +29,6 @@ constexpr int kHeadsPerUnit = 4;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp64 -> bf16, round to nearest even, in one step. The fp32 rounding is
-// exact unless the fp32 result sits exactly half-way between two bf16 values
-// while the fp64 value does not; then the tie is broken by the side the fp64
-// value lies on (finite inputs only).
-__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
-  const float f = (float)x;
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0xFFFFu) == 0x8000u && (double)f != x) {
-    const bool away = fabs(x) > fabs((double)f);
-    u = away ? u + 1u : u - 1u;
-  }
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 template <int D>
 __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
   constexpr int LPR = D / 8;
@@ -127,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
       const double y1 = x[2 * e + 1] * inv * (double)g[t][2 * e + 1];
       const double r0 = y0 * cs[e] - y1 * sn[e];
       const double r1 = y0 * sn[e] + y1 * cs[e];
-      o[e] = f64_to_bf16(r0) | (f64_to_bf16(r1) << 16);
+      o[e] = f64_to_bf16_rne(r0) | (f64_to_bf16_rne(r1) << 16);
     }
     uint16_t* out = t ? p.k_out : p.q_out;
     if (active && hi < nh)

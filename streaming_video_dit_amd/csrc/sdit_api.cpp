@@ -415,6 +415,79 @@ SDIT_API int sdit_window_permute(const void* x, void* y, int32_t T, int32_t Hl, 
   return device_status(sdit::launch_window_permute(P, (hipStream_t)stream), "window_permute");
 }
 
+// ------------------------------------------------------------------ rmsnorm / layernorm_modulate
+
+namespace {
+
+// x, y bf16 [n_tok][dim]; vec[0..n_vec) fp32 [dim] each.
+int fill_norm_params(const char* fn, const void* x, const void* y, const float* const* vec, int n_vec,
+                     int64_t n_tok, int32_t dim, float eps, sdit::NormParams* P) {
+  if (dim < 8 || dim > SDIT_MAX_NORM_DIM || dim % 8 != 0)
+    return fail(SDIT_ERR_UNSUPPORTED, "%s: dim %d is not a multiple of 8 in [8, %d]", fn, dim, SDIT_MAX_NORM_DIM);
+  // one 64-lane wave per token; a launch holds fewer than 2^32 threads
+  if (n_tok < 0 || n_tok >= ((int64_t)1 << 26))
+    return fail(SDIT_ERR_INVALID, "%s: n_tok %lld outside [0, 2^26)", fn, (long long)n_tok);
+  if (!(eps >= 0.0f) || eps > 1.0f) return fail(SDIT_ERR_INVALID, "%s: eps must be in [0, 1]", fn);
+  if (n_tok > 0) {
+    const int64_t bytes = n_tok * dim * 2;
+    if (x == nullptr || y == nullptr || !aligned(x, 16) || !aligned(y, 16))
+      return fail(SDIT_ERR_INVALID, "%s: x and y must be non-NULL, 16-byte aligned", fn);
+    if (y != x && overlap(x, bytes, y, bytes))
+      return fail(SDIT_ERR_INVALID, "%s: y overlaps x (only exact in-place is allowed)", fn);
+    for (int i = 0; i < n_vec; ++i) {
+      if (vec[i] == nullptr || !aligned(vec[i], 16))
+        return fail(SDIT_ERR_INVALID, "%s: parameter vectors must be non-NULL, 16-byte aligned", fn);
+      if (overlap(y, bytes, vec[i], (int64_t)dim * 4))
+        return fail(SDIT_ERR_INVALID, "%s: y overlaps a parameter vector", fn);
+    }
+  }
+  if (P != nullptr) {
+    P->x = (const uint16_t*)x;
+    P->y = (uint16_t*)y;
+    P->gamma = n_vec == 1 ? vec[0] : nullptr;
+    P->scale = n_vec == 2 ? vec[0] : nullptr;
+    P->shift = n_vec == 2 ? vec[1] : nullptr;
+    P->n_tok = n_tok;
+    P->dim = dim;
+    P->eps = eps;
+  }
+  return ok();
+}
+
+}  // namespace
+
+SDIT_API int sdit_validate_rmsnorm_args(const void* x, const void* y, const float* gamma, int64_t n_tok, int32_t dim,
+                                        float eps) {
+  const float* vec[1] = {gamma};
+  return fill_norm_params("rmsnorm", x, y, vec, 1, n_tok, dim, eps, nullptr);
+}
+
+SDIT_API int sdit_rmsnorm(const void* x, void* y, const float* gamma, int64_t n_tok, int32_t dim, float eps,
+                          void* stream) {
+  const float* vec[1] = {gamma};
+  sdit::NormParams P;
+  int st = fill_norm_params("rmsnorm", x, y, vec, 1, n_tok, dim, eps, &P);
+  if (st != SDIT_OK) return st;
+  if (n_tok == 0) return ok();
+  return device_status(sdit::launch_rmsnorm(P, (hipStream_t)stream), "rmsnorm");
+}
+
+SDIT_API int sdit_validate_layernorm_modulate_args(const void* x, const void* y, const float* scale,
+                                                   const float* shift, int64_t n_tok, int32_t dim, float eps) {
+  const float* vec[2] = {scale, shift};
+  return fill_norm_params("layernorm_modulate", x, y, vec, 2, n_tok, dim, eps, nullptr);
+}
+
+SDIT_API int sdit_layernorm_modulate(const void* x, void* y, const float* scale, const float* shift, int64_t n_tok,
+                                     int32_t dim, float eps, void* stream) {
+  const float* vec[2] = {scale, shift};
+  sdit::NormParams P;
+  int st = fill_norm_params("layernorm_modulate", x, y, vec, 2, n_tok, dim, eps, &P);
+  if (st != SDIT_OK) return st;
+  if (n_tok == 0) return ok();
+  return device_status(sdit::launch_layernorm_modulate(P, (hipStream_t)stream), "layernorm_modulate");
+}
+
 SDIT_API int sdit_attn_fwd(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs,
                            const uint8_t* block_mask, int32_t block_q, int32_t block_k, int32_t n_heads,
                            int32_t head_dim, float softmax_scale, void* out, float* lse, void* stream) {

@@ -8,6 +8,22 @@ namespace sdit {
 
 constexpr int kMaxSegments = 8;
 
+// fp64 -> bf16, round to nearest even, in one step. The fp32 rounding is
+// exact unless the fp32 result sits exactly half-way between two bf16 values
+// while the fp64 value does not; then the tie is broken by the side the fp64
+// value lies on (finite inputs only).
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
+  const float f = (float)x;
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0xFFFFu) == 0x8000u && (double)f != x) {
+    const bool away = fabs(x) > fabs((double)f);
+    u = away ? u + 1u : u - 1u;
+  }
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+
 // ---------------------------------------------------------------- qknorm_rope3d
 struct RopeParams {
   const uint16_t* q_in;
@@ -89,5 +105,19 @@ struct PermuteParams {
   int64_t n_tok;
 };
 hipError_t launch_window_permute(const PermuteParams& p, hipStream_t stream);
+
+// ---------------------------------------------------------------- rmsnorm / layernorm_modulate
+struct NormParams {
+  const uint16_t* x;
+  uint16_t* y;
+  const float* gamma;   // rmsnorm
+  const float* scale;   // layernorm_modulate
+  const float* shift;
+  int64_t n_tok;
+  int32_t dim;
+  float eps;
+};
+hipError_t launch_rmsnorm(const NormParams& p, hipStream_t stream);
+hipError_t launch_layernorm_modulate(const NormParams& p, hipStream_t stream);
 
 }  // namespace sdit

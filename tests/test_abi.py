@@ -183,6 +183,43 @@ def test_window_permute_validation():
     assert v(n_heads=0) == sdit.SDIT_ERR_INVALID
 
 
+def test_norm_validation():
+    x, y = A16, A16 + 512 * MB            # 32760 tokens x 5120 bf16 = 335 MB each
+    g, sh = A16 + 1024 * MB, A16 + 1025 * MB
+
+    def rms(**kw):
+        a = dict(x=x, y=y, gamma=g, n_tok=32760, dim=5120, eps=1e-6)
+        a.update(kw)
+        return sdit.validate_rmsnorm_args(**a)
+
+    def ln(**kw):
+        a = dict(x=x, y=y, scale=g, shift=sh, n_tok=32760, dim=5120, eps=1e-6)
+        a.update(kw)
+        return sdit.validate_layernorm_modulate_args(**a)
+
+    for v in (rms, ln):
+        assert v() == sdit.SDIT_OK
+        assert v(y=x) == sdit.SDIT_OK                    # exact in place
+        assert v(y=x + 1024) == sdit.SDIT_ERR_INVALID    # partial overlap
+        assert v(y=y + 8) == sdit.SDIT_ERR_INVALID       # misaligned
+        assert v(x=None) == sdit.SDIT_ERR_INVALID
+        assert v(dim=5124) == sdit.SDIT_ERR_UNSUPPORTED  # not a multiple of 8
+        assert v(dim=8200) == sdit.SDIT_ERR_UNSUPPORTED  # above SDIT_MAX_NORM_DIM
+        assert v(dim=8192) == sdit.SDIT_OK
+        assert v(dim=0) == sdit.SDIT_ERR_UNSUPPORTED
+        assert v(n_tok=-1) == sdit.SDIT_ERR_INVALID
+        assert v(n_tok=1 << 26) == sdit.SDIT_ERR_INVALID
+        assert v(n_tok=0, x=None, y=None) == sdit.SDIT_OK
+        assert v(eps=-1.0) == sdit.SDIT_ERR_INVALID
+        assert v(eps=float("nan")) == sdit.SDIT_ERR_INVALID
+    assert rms(gamma=None) == sdit.SDIT_ERR_INVALID
+    assert rms(gamma=g + 4) == sdit.SDIT_ERR_INVALID
+    assert rms(gamma=y + 4096) == sdit.SDIT_ERR_INVALID  # output overlaps gamma
+    assert ln(shift=None) == sdit.SDIT_ERR_INVALID
+    assert ln(scale=y) == sdit.SDIT_ERR_INVALID
+    assert "layernorm_modulate" in (ln(dim=12), sdit.last_error())[1]
+
+
 def test_error_message_is_per_call():
     sdit.validate_kv_quant_args(A16, A16 + 8, A16 + 32 * MB, 100, 12, 128)
     assert sdit.last_error() != ""

@@ -33,6 +33,7 @@ TID_TEXT_K, TID_TEXT_V = 3, 4
 TID_HIST_K, TID_HIST_V = 5, 6
 TID_GAMMA_Q, TID_GAMMA_K = 7, 8
 TID_K_OUTLIER, TID_V_OUTLIER = 9, 10
+TID_HIDDEN, TID_CH_SCALE, TID_TOK_OFFSET, TID_GAMMA, TID_MOD_SCALE, TID_MOD_SHIFT = 11, 12, 13, 14, 15, 16
 TID_TILE_MASK = 100
 
 
@@ -281,3 +282,31 @@ def attn_flops(cfg: Config, mask: np.ndarray) -> int:
     cols = np.array(cols, dtype=np.int64)
     kept = (mask != 0).astype(np.int64)
     return int(4 * cfg.head_dim * cfg.n_heads * (rows[:, None] * cols[None, :] * kept).sum())
+
+
+@dataclass
+class NormInputs:
+    x: np.ndarray        # bf16 bits [n_tok, dim]
+    gamma: np.ndarray    # fp32 [dim]   (RMSNorm gain)
+    scale: np.ndarray    # fp32 [dim]   (modulation scale)
+    shift: np.ndarray    # fp32 [dim]   (modulation shift)
+
+
+def make_norm_inputs(seed: int, n_tok: int, dim: int, offset: float = 0.0) -> NormInputs:
+    """Hidden-state-like rows for the per-token norms: N(0,1) per element
+    times a per-channel magnitude (log-uniform over [1/4, 4], and 1 channel
+    in 64 at 32x: DiT activations carry a few large channels), plus a
+    per-token offset drawn from N(0, offset^2); gamma U(0.5, 1.5), the
+    modulation scale U(-0.5, 0.5) and shift U(-1, 1)."""
+    rng = np.random.default_rng([seed, TID_HIDDEN])
+    x = rng.standard_normal(size=(n_tok, dim))
+    crng = np.random.default_rng([seed, TID_CH_SCALE])
+    ch = np.exp2(crng.uniform(-2.0, 2.0, size=dim))
+    ch = np.where(crng.random(size=dim) < 1.0 / 64, 32.0, ch)
+    x = x * ch
+    if offset:
+        x = x + np.random.default_rng([seed, TID_TOK_OFFSET]).normal(0.0, offset, size=(n_tok, 1))
+    return NormInputs(x=_f32_to_bf16_bits(x.astype(np.float32)),
+                      gamma=uniform_f32(seed, TID_GAMMA, (dim,), 0.5, 1.5),
+                      scale=uniform_f32(seed, TID_MOD_SCALE, (dim,), -0.5, 0.5),
+                      shift=uniform_f32(seed, TID_MOD_SHIFT, (dim,), -1.0, 1.0))
