@@ -9,15 +9,17 @@
 // by every token), rounded to bf16 once.
 //
 // HBM-bound: 2 * C bytes in and 2 * C bytes out per token; the fp32 vectors
-// (4 or 8 bytes per column) are read by every row but stay in L2. One wave
-// owns one row: lane l holds 16-byte chunks l, l + 64, l + 128, ... of it in
-// registers (every load of the row is issued before the first reduction, and
-// each load instruction covers 1 KB of contiguous row), so x is read from HBM
-// once however many passes the statistics take. The arithmetic is fp64 with
+// (4 or 8 bytes per column) are read by every row but stay in L2. A wave
+// owns one row at a time: lane l holds 16-byte chunks l, l + 64, l + 128, ...
+// of it in registers (every load of the row is issued before the first
+// reduction, and each load instruction covers 1 KB of contiguous row), so x
+// is read from HBM once however many passes the statistics take. The arithmetic is fp64 with
 // one correctly rounded fp64 -> bf16 conversion at the end: in fp32, x - mean
 // of a row whose mean is large against its spread loses bits of the small
 // difference; in fp64 every output is within one bf16 ulp of the exact value.
 #include "sdit_internal.h"
+
+#include <algorithm>
 
 namespace sdit {
 namespace {
@@ -25,6 +27,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = kThreads / 64;
 constexpr int kMaxChunksPerLane = 16;   // C <= 16 * 64 * 8 = 8192
+constexpr int kDirectMaxChunks = 4;     // one row per wave up to C = 2048
+constexpr int64_t kPipeMaxBlocks = 256 * 8;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -35,46 +39,53 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-__device__ __forceinline__ void load_f8(const float* base, int c0, float (&g)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(base + c0);
-  const float4 b = *reinterpret_cast<const float4*>(base + c0 + 4);
-  g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
-  g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
+// An empty asm that the compiler must assume rewrites w: the fp64 values
+// derived from the row are then recomputed in each pass instead of being kept
+// in registers across the reductions (16 registers per chunk).
+__device__ __forceinline__ void launder(uint32_t (&w)[4]) {
+  asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
 }
 
-// K = chunks per lane (ceil(C / 8 / 64)); chunks past C / 8 are idle.
-template <int K, bool LN>
-__global__ __launch_bounds__(kThreads) void norm_kernel(NormParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= p.n_tok) return;   // whole waves leave together
-  const int n_chunks = p.dim >> 3;
-  const uint4* x = reinterpret_cast<const uint4*>(p.x + row * p.dim);
+template <bool LAUNDER>
+__device__ __forceinline__ void unpack(const uint4& r, uint32_t (&w)[4]) {
+  w[0] = r.x; w[1] = r.y; w[2] = r.z; w[3] = r.w;
+  if constexpr (LAUNDER) launder(w);
+}
 
-  uint4 raw[K];
+template <int K>
+__device__ __forceinline__ void load_row(const uint16_t* base, int64_t row, int dim, int lane, uint4 (&r)[K]) {
+  const uint4* x = reinterpret_cast<const uint4*>(base + row * dim);
+  const int n_chunks = dim >> 3;
 #pragma unroll
   for (int i = 0; i < K; ++i) {
     const int c = lane + 64 * i;
-    raw[i] = c < n_chunks ? x[c] : make_uint4(0, 0, 0, 0);
+    r[i] = c < n_chunks ? x[c] : make_uint4(0, 0, 0, 0);
   }
+}
 
-  // Unused chunks hold +0, which adds nothing to either sum; the centred
-  // pass below masks them explicitly.
-  double mean = 0.0, inv;
+// Row statistics in fp64: the mean (LayerNorm) and 1 / sqrt(mean square or
+// population variance + eps). Unused chunks hold +0, which adds nothing to
+// the sums; the centred pass masks them explicitly.
+template <int K, bool LN, bool LAUNDER>
+__device__ __forceinline__ void row_stats(const uint4 (&raw)[K], int lane, int n_chunks, int dim, float eps,
+                                          double& mean, double& inv) {
+  mean = 0.0;
+  double ss = 0.0;
   if constexpr (LN) {
     double s = 0.0;
 #pragma unroll
     for (int i = 0; i < K; ++i) {
-      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      uint32_t w[4];
+      unpack<LAUNDER>(raw[i], w);
 #pragma unroll
       for (int e = 0; e < 4; ++e) s += (double)bf16_lo(w[e]) + (double)bf16_hi(w[e]);
     }
-    mean = wave_sum(s) / (double)p.dim;
-    double ss = 0.0;
+    mean = wave_sum(s) / (double)dim;
 #pragma unroll
     for (int i = 0; i < K; ++i) {
       if (lane + 64 * i >= n_chunks) continue;
-      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      uint32_t w[4];
+      unpack<LAUNDER>(raw[i], w);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const double d0 = (double)bf16_lo(w[e]) - mean, d1 = (double)bf16_hi(w[e]) - mean;
@@ -82,12 +93,11 @@ __global__ __launch_bounds__(kThreads) void norm_kernel(NormParams p) {
         ss = fma(d1, d1, ss);
       }
     }
-    inv = 1.0 / sqrt(wave_sum(ss) / (double)p.dim + (double)p.eps);
   } else {
-    double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < K; ++i) {
-      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      uint32_t w[4];
+      unpack<LAUNDER>(raw[i], w);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const double a = bf16_lo(w[e]), b = bf16_hi(w[e]);
@@ -95,37 +105,96 @@ __global__ __launch_bounds__(kThreads) void norm_kernel(NormParams p) {
         ss = fma(b, b, ss);
       }
     }
-    inv = 1.0 / sqrt(wave_sum(ss) / (double)p.dim + (double)p.eps);
   }
+  inv = 1.0 / sqrt(wave_sum(ss) / (double)dim + (double)eps);
+}
 
-  uint4* y = reinterpret_cast<uint4*>(p.y + row * p.dim);
+// The 8 outputs of one chunk, fp64, one correctly rounded conversion each.
+// ga / sh point at the chunk's 8 gamma (or scale) and shift values.
+template <bool LN, bool LAUNDER>
+__device__ __forceinline__ uint4 norm_chunk(const uint4& raw, double mean, double inv, const float* ga,
+                                            const float* sh) {
+  float g[8], b[8];
+  *reinterpret_cast<float4*>(g) = *reinterpret_cast<const float4*>(ga);
+  *reinterpret_cast<float4*>(g + 4) = *reinterpret_cast<const float4*>(ga + 4);
+  if constexpr (LN) {
+    *reinterpret_cast<float4*>(b) = *reinterpret_cast<const float4*>(sh);
+    *reinterpret_cast<float4*>(b + 4) = *reinterpret_cast<const float4*>(sh + 4);
+  }
+  uint32_t w[4];
+  unpack<LAUNDER>(raw, w);
+  uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < K; ++i) {
-    const int c = lane + 64 * i;
-    if (c >= n_chunks) continue;
-    float ga[8], sh[8];
-    if constexpr (LN) {
-      load_f8(p.scale, 8 * c, ga);
-      load_f8(p.shift, 8 * c, sh);
-    } else {
-      load_f8(p.gamma, 8 * c, ga);
+  for (int e = 0; e < 4; ++e) {
+    double v[2] = {bf16_lo(w[e]), bf16_hi(w[e])};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = 2 * e + h;
+      if constexpr (LN)
+        v[h] = fma((v[h] - mean) * inv, 1.0 + (double)g[j], (double)b[j]);
+      else
+        v[h] = v[h] * inv * (double)g[j];
     }
-    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-    uint32_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      double v[2] = {bf16_lo(w[e]), bf16_hi(w[e])};
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int j = 2 * e + h;
-        if constexpr (LN)
-          v[h] = fma((v[h] - mean) * inv, 1.0 + (double)ga[j], (double)sh[j]);
-        else
-          v[h] = v[h] * inv * (double)ga[j];
+    o[e] = f64_to_bf16_rne(v[0]) | (f64_to_bf16_rne(v[1]) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// K = chunks per lane (ceil(C / 8 / 64)); chunks past C / 8 are idle.
+//
+// Up to 4 chunks per lane (C <= 2048) every wave takes one row and the grid
+// covers all rows: registers stay few, so many rows are in flight per CU.
+// Above that (PIPE) the row no longer fits that way: a wave walks rows
+// row, row + W, row + 2W, ... (W waves in the grid) and issues the loads of
+// its next row before it reduces the current one, the fp32 vectors are
+// staged in LDS once per workgroup (their reads then wait on the LDS
+// counter, not behind the next row's global loads), and each pass re-derives
+// its fp64 values from the packed row.
+template <int K, bool LN>
+__global__ __launch_bounds__(kThreads) void norm_kernel(NormParams p) {
+  constexpr bool PIPE = K > kDirectMaxChunks;
+  extern __shared__ float4 vec_lds[];   // PIPE: gamma, or scale then shift, fp32 [dim] each
+  if constexpr (PIPE) {
+    const int n_vec4 = p.dim >> 2;
+    for (int i = threadIdx.x; i < n_vec4; i += kThreads) {
+      if constexpr (LN) {
+        vec_lds[i] = reinterpret_cast<const float4*>(p.scale)[i];
+        vec_lds[n_vec4 + i] = reinterpret_cast<const float4*>(p.shift)[i];
+      } else {
+        vec_lds[i] = reinterpret_cast<const float4*>(p.gamma)[i];
       }
-      o[e] = f64_to_bf16_rne(v[0]) | (f64_to_bf16_rne(v[1]) << 16);
     }
-    y[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    __syncthreads();
+  }
+  const float* ga = PIPE ? reinterpret_cast<const float*>(vec_lds) : (LN ? p.scale : p.gamma);
+  const float* sh = PIPE ? reinterpret_cast<const float*>(vec_lds) + p.dim : p.shift;
+
+  const int lane = threadIdx.x & 63;
+  const int n_chunks = p.dim >> 3;
+  const int64_t stride = (int64_t)gridDim.x * kRowsPerBlock;
+  int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= p.n_tok) return;   // whole waves leave together
+
+  uint4 raw[K];
+  load_row<K>(p.x, row, p.dim, lane, raw);
+  for (;;) {
+    const int64_t next = row + stride;
+    const bool more = PIPE && next < p.n_tok;
+    uint4 nxt[K];
+    if (more) load_row<K>(p.x, next, p.dim, lane, nxt);
+
+    double mean, inv;
+    row_stats<K, LN, PIPE>(raw, lane, n_chunks, p.dim, p.eps, mean, inv);
+    uint4* y = reinterpret_cast<uint4*>(p.y + row * p.dim);
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const int c = lane + 64 * i;
+      if (c < n_chunks) y[c] = norm_chunk<LN, PIPE>(raw[i], mean, inv, ga + 8 * c, sh + 8 * c);
+    }
+    if (!more) break;
+#pragma unroll
+    for (int i = 0; i < K; ++i) raw[i] = nxt[i];
+    row = next;
   }
 }
 
@@ -133,11 +202,16 @@ template <bool LN>
 hipError_t launch_norm(const NormParams& p, hipStream_t stream) {
   if (p.n_tok == 0) return hipSuccess;
   const int k = (p.dim / 8 + 63) / 64;
-  const int64_t blocks = (p.n_tok + kRowsPerBlock - 1) / kRowsPerBlock;
+  const bool pipe = k > kDirectMaxChunks;
+  // direct: one row per wave; pipelined: a few workgroups per CU, each wave
+  // walking about n_tok / (4 * blocks) rows
+  int64_t blocks = (p.n_tok + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (pipe) blocks = std::min<int64_t>(blocks, kPipeMaxBlocks);
+  const size_t lds = pipe ? (size_t)p.dim * sizeof(float) * (LN ? 2 : 1) : 0;
   const dim3 grid((unsigned)blocks), block(kThreads);
   switch (k) {
 #define SDIT_NORM_CASE(K) \
-  case K: hipLaunchKernelGGL((norm_kernel<K, LN>), grid, block, 0, stream, p); break;
+  case K: hipLaunchKernelGGL((norm_kernel<K, LN>), grid, block, lds, stream, p); break;
     SDIT_NORM_CASE(1) SDIT_NORM_CASE(2) SDIT_NORM_CASE(3) SDIT_NORM_CASE(4)
     SDIT_NORM_CASE(5) SDIT_NORM_CASE(6) SDIT_NORM_CASE(7) SDIT_NORM_CASE(8)
     SDIT_NORM_CASE(9) SDIT_NORM_CASE(10) SDIT_NORM_CASE(11) SDIT_NORM_CASE(12)

@@ -73,10 +73,23 @@ def test_norm_within_one_ulp(op, n_tok, dim):
     _check(_run(op, inp), _ref(op, inp))
 
 
+# Above 2048 columns each wave walks several rows (one workgroup per 4 rows up
+# to 2048 workgroups): 16421 rows = 2.005 rows per wave, so most waves take
+# two rows and a few take three; every row is checked.
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("dim", [2560, 8192])
+def test_norm_rows_walked_per_wave(op, dim):
+    n = 2 * 8192 + 37 if dim == 2560 else 8192 + 5
+    inp = W.make_norm_inputs(46, n, dim, offset=1.0)
+    _say(op, n, dim)
+    _check(_run(op, inp), _ref(op, inp))
+
+
 @pytest.mark.parametrize("op", OPS)
 def test_norm_in_place_equals_out_of_place(op):
-    inp = W.make_norm_inputs(41, 77, 1536)
-    assert np.array_equal(_run(op, inp), _run(op, inp, in_place=True))
+    for n, d in ((77, 1536), (8200, 4096)):
+        inp = W.make_norm_inputs(41, n, d)
+        assert np.array_equal(_run(op, inp), _run(op, inp, in_place=True))
 
 
 @pytest.mark.parametrize("op", OPS)
