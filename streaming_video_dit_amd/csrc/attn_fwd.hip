@@ -24,10 +24,19 @@
 //    into LDS (global_load_lds_dwordx4: lane t lands at base + 16 t, so each
 //    lane's source address is chosen to realise the padded layout below). V
 //    is staged through registers and converted to fp16; int8 K/V codes are
-//    widened exactly on the same path. Each wave's share of the next tile's
-//    loads is issued between its score MFMAs rather than all at once (a
-//    burst from every wave queues in the CU's address unit and stalls the
-//    issuing waves).
+//    widened exactly on the same path. Each wave's share of a tile's
+//    register loads is issued between its score MFMAs rather than all at
+//    once (a burst from every wave queues in the CU's address unit and
+//    stalls the issuing waves).
+//  * Who moves the tiles differs by kernel. Without int8 segments the four
+//    leading waves load and stage every tile one step ahead (the lagging
+//    waves are the critical path there). With int8 segments all eight waves
+//    stage (the int8 tiles need the registers), two steps ahead: each wave
+//    commits its share of tile i+1 in step i, the leading waves first (then
+//    scores, softmax, P.V: vector, matrix, vector, matrix), the lagging ones
+//    between their P.V of tile i-1 and their scores of tile i (matrix,
+//    vector, matrix, vector), so on every SIMD the two waves alternate
+//    between the matrix and the vector units.
 //  * LDS tiles are row-major ([key][d]) with padded rows: K rows are D+8
 //    bf16 (16 rows read at one column land on 16 different 4-bank groups), V
 //    rows are D+32 fp16 (the 4 rows x 64 bytes that one transposed read
@@ -114,17 +123,27 @@ struct Layout {
   static_assert(BK * K_CH % 64 == 0, "K tile must be whole 64-lane blocks");
 };
 
-// Who moves a tile: the first LW waves of the workgroup (LT threads).
-template <int D, int LW>
+// Who moves a tile. bf16 K goes from global memory straight into LDS,
+// issued by the first KW waves (the ones that run ahead). V (bf16 -> fp16)
+// and int8 K/V codes are staged through the registers of the first ST
+// threads: the four leading waves in unscaled kernels (there the lagging
+// waves are the critical path), all eight waves in scaled kernels (the
+// staged int8 tiles need the registers).
+template <int D, int ST>
 struct Loader {
-  static constexpr int LT = LW * 64;
-  static constexpr int VCH = BK * Layout<D>::CPR / LT;  // bf16 V chunks staged per thread
+  static constexpr int KW = NW / 2;
+  static constexpr int VCH = BK * Layout<D>::CPR / ST;  // bf16 V chunks staged per thread
   static constexpr int I8_THREADS = BK * (D / 16);      // threads moving 16 int8 codes of K and of V
-  static constexpr int I8CH = I8_THREADS >= LT ? I8_THREADS / LT : 1;
-  static constexpr int SR = VCH > 2 * I8CH ? VCH : 2 * I8CH;
-  static constexpr int KMAX = (Layout<D>::K_BLKS + LW - 1) / LW;   // direct-load blocks per wave
-  static_assert(VCH >= 1 && BK * Layout<D>::CPR % LT == 0, "V tile must be whole chunks per thread");
-  static_assert(I8_THREADS % LT == 0 || I8_THREADS < LT, "int8 tile split");
+  static constexpr int I8CH = I8_THREADS >= ST ? I8_THREADS / ST : 1;
+  static constexpr int KMAX = (Layout<D>::K_BLKS + KW - 1) / KW;   // direct-load blocks per K wave
+  // staged registers and one-instruction load parts per tile (scaled kernels
+  // also stage int8 tiles: K codes, V codes, then the per-key scales)
+  template <bool SCALED>
+  static constexpr int sr() { return SCALED && 2 * I8CH > VCH ? 2 * I8CH : VCH; }
+  template <bool SCALED>
+  static constexpr int npart() { return SCALED && 2 * I8CH + 1 > VCH ? 2 * I8CH + 1 : VCH; }
+  static_assert(VCH >= 1 && BK * Layout<D>::CPR % ST == 0, "V tile must be whole chunks per thread");
+  static_assert(I8_THREADS % ST == 0 || I8_THREADS < ST, "int8 tile split");
 };
 
 template <int D>
@@ -239,30 +258,32 @@ __device__ __forceinline__ uint4 i8x8_to_f16x8(uint32_t w0, uint32_t w1) {
 
 // Registers holding the register-staged part of one tile between its global
 // load and its LDS store. bf16 tiles: VCH chunks of 8 V values. int8 tiles:
-// I8CH chunks of 16 K codes, then I8CH chunks of 16 V codes.
-template <int D, int LW>
+// I8CH chunks of 16 K codes, then I8CH chunks of 16 V codes, and the raw
+// per-key scales.
+template <int D, int ST, bool SCALED>
 struct Stage {
-  uint4 r[Loader<D, LW>::SR];
+  uint4 r[Loader<D, ST>::template sr<SCALED>()];
   float ks, vs;
 };
 
 // Per-thread load geometry, fixed for the whole kernel: element offsets (from
 // a tile's first row, head included) of every chunk this thread moves.
-template <int D, int LW>
+template <int D, int ST>
 struct LoadPlan {
-  static constexpr int KMAX = Loader<D, LW>::KMAX;
-  int k_off[KMAX];   // bf16 K, padded-tile block wave + LW*i (padding chunks reload chunk 0)
-  int v_off;         // bf16 V chunk j adds j * (LT / CPR) rows
-  int i8_off;        // int8 K/V chunk j adds j * (LT / (D/16)) rows
+  static constexpr int KMAX = Loader<D, ST>::KMAX;
+  int k_off[KMAX];   // bf16 K (K waves), padded-tile block wave + KW*i (padding chunks reload chunk 0)
+  int v_off;         // bf16 V chunk j adds j * (ST / CPR) rows
+  int i8_off;        // int8 K/V chunk j adds j * (ST / (D/16)) rows
 };
 
-template <int D, int LW>
-__device__ __forceinline__ void make_plan(LoadPlan<D, LW>& pl, int row_stride) {
+template <int D, int ST>
+__device__ __forceinline__ void make_plan(LoadPlan<D, ST>& pl, int row_stride) {
   using L = Layout<D>;
+  constexpr int KW = Loader<D, ST>::KW;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-  for (int i = 0; i < LoadPlan<D, LW>::KMAX; ++i) {
-    const int lin = (wave + LW * i) * 64 + lane;
+  for (int i = 0; i < LoadPlan<D, ST>::KMAX; ++i) {
+    const int lin = (wave + KW * i) * 64 + lane;
     const int row = lin / L::K_CH, pc = lin % L::K_CH;
     pl.k_off[i] = row * row_stride + (pc < L::CPR ? pc : 0) * 8;
   }
@@ -270,71 +291,69 @@ __device__ __forceinline__ void make_plan(LoadPlan<D, LW>& pl, int row_stride) {
   pl.i8_off = (tid / (D / 16)) * row_stride + (tid % (D / 16)) * 16;
 }
 
-// Loads of one tile, cut into NPART pieces of one or two wave instructions
-// each so that they can be spread over a wave's matrix work (every wave
-// issuing a whole tile at once queues its instructions behind the other
-// waves' in the CU's address unit). bf16 tiles: K goes directly into LDS
-// buffer kbuf, V into registers (finished by commit_tile). int8 tiles: K and
-// V codes into registers, then the per-key scales. Rows past the segment end
-// are loaded from its last row: their scores get the -1e30 bias, so their
-// probabilities are exactly 0 and any finite data there is harmless.
-template <int D, int LW>
-struct TileLoad {
-  static constexpr int KMAX = Loader<D, LW>::KMAX;
-  static constexpr int NB16 = KMAX + Loader<D, LW>::VCH;
-  static constexpr int NI8 = 2 * Loader<D, LW>::I8CH + 1;
-  static constexpr int NPART = NB16 > NI8 ? NB16 : NI8;
-};
-
-template <int D, bool SCALED, int LW>
-__device__ __forceinline__ void issue_part(const AttnParams& p, const TileRef& t, int head, Stage<D, LW>& st,
-                                           Smem<D>& sm, int kbuf, const LoadPlan<D, LW>& pl, int j) {
+// bf16 K of tile t straight into LDS buffer kbuf (K waves only). Rows past
+// the segment end are loaded from its last row: their scores get the -1e30
+// bias, so their probabilities are exactly 0 and any finite data there is
+// harmless.
+template <int D, int ST>
+__device__ __forceinline__ void issue_kdma(const AttnParams& p, const TileRef& t, int head, Smem<D>& sm, int kbuf,
+                                           const LoadPlan<D, ST>& pl) {
   using L = Layout<D>;
-  using LD = Loader<D, LW>;
-  constexpr int LT = LD::LT;
+  constexpr int KW = Loader<D, ST>::KW;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row_stride = p.n_heads * D;
+  const uint16_t* kb = (const uint16_t*)t.k + ((int64_t)t.key0 * p.n_heads + head) * D;
+  const bool ragged = t.n_valid < BK;
+#pragma unroll
+  for (int j = 0; j < Loader<D, ST>::KMAX; ++j) {
+    const int blk = wave + KW * j;
+    if (blk < L::K_BLKS) {
+      int off = pl.k_off[j];
+      if (ragged) {
+        const int lin = blk * 64 + lane;
+        const int row = lin / L::K_CH, pc = lin % L::K_CH;
+        off = min(row, t.n_valid - 1) * row_stride + (pc < L::CPR ? pc : 0) * 8;
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(kb + off), (lds_void*)(sm.k[kbuf] + blk * 64 * 8), 16, 0, 0);
+    }
+  }
+}
+
+// Register-staged loads of tile t, cut into NPART one-instruction parts so
+// that they can ride on a wave's matrix work (a burst from every wave queues
+// in the CU's address unit). bf16 tiles: V chunks. int8 tiles: K codes, V
+// codes, then the raw per-key scales (commit_tile turns them into
+// multipliers; using them here would wait for the loads).
+template <int D, int ST, bool SCALED>
+__device__ __forceinline__ void issue_stage_part(const AttnParams& p, const TileRef& t, int head,
+                                                 Stage<D, ST, SCALED>& st, const LoadPlan<D, ST>& pl, int j) {
+  using L = Layout<D>;
+  using LD = Loader<D, ST>;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int row_stride = p.n_heads * D;   // elements between consecutive tokens
+  const int row_stride = p.n_heads * D;
   const int64_t base = ((int64_t)t.key0 * p.n_heads + head) * D;
   const bool ragged = t.n_valid < BK;
   if (!SCALED || !t.is_int8) {
-    const uint16_t* kb = (const uint16_t*)t.k + base;
-    const uint16_t* vb = (const uint16_t*)t.v + base;
-    if (j < TileLoad<D, LW>::KMAX) {
-      const int blk = wave + LW * j;
-      if (blk < L::K_BLKS) {
-        int off = pl.k_off[j];
-        if (ragged) {
-          const int lin = blk * 64 + lane;
-          const int row = lin / L::K_CH, pc = lin % L::K_CH;
-          off = min(row, t.n_valid - 1) * row_stride + (pc < L::CPR ? pc : 0) * 8;
-        }
-        __builtin_amdgcn_global_load_lds((const void*)(kb + off), (lds_void*)(sm.k[kbuf] + blk * 64 * 8), 16, 0, 0);
-      }
-    } else if (j < TileLoad<D, LW>::NB16) {
-      const int jv = j - TileLoad<D, LW>::KMAX;
-      constexpr int RSTEP = LT / L::CPR;
-      int off = pl.v_off + jv * RSTEP * row_stride;
-      if (ragged) off = min(tid / L::CPR + jv * RSTEP, t.n_valid - 1) * row_stride + (tid % L::CPR) * 8;
-      st.r[jv] = *reinterpret_cast<const uint4*>(vb + off);
+    if (j < LD::VCH) {
+      const uint16_t* vb = (const uint16_t*)t.v + base;
+      constexpr int RSTEP = ST / L::CPR;
+      int off = pl.v_off + j * RSTEP * row_stride;
+      if (ragged) off = min(tid / L::CPR + j * RSTEP, t.n_valid - 1) * row_stride + (tid % L::CPR) * 8;
+      st.r[j] = *reinterpret_cast<const uint4*>(vb + off);
     }
   } else {
-    const int8_t* kb = (const int8_t*)t.k + base;
-    const int8_t* vb = (const int8_t*)t.v + base;
     if (j < 2 * LD::I8CH) {
-      if (LD::I8_THREADS >= LT || tid < LD::I8_THREADS) {
+      if (LD::I8_THREADS >= ST || tid < LD::I8_THREADS) {
         const int ji = j % LD::I8CH;
-        constexpr int RSTEP = LT / (D / 16);
+        constexpr int RSTEP = ST / (D / 16);
         int off = pl.i8_off + ji * RSTEP * row_stride;
         if (ragged) off = min(tid / (D / 16) + ji * RSTEP, t.n_valid - 1) * row_stride + (tid % (D / 16)) * 16;
         if (j < LD::I8CH)
-          st.r[ji] = *reinterpret_cast<const uint4*>(kb + off);
+          st.r[ji] = *reinterpret_cast<const uint4*>((const int8_t*)t.k + base + off);
         else
-          st.r[LD::I8CH + ji] = *reinterpret_cast<const uint4*>(vb + off);
+          st.r[LD::I8CH + ji] = *reinterpret_cast<const uint4*>((const int8_t*)t.v + base + off);
       }
     } else if (j == 2 * LD::I8CH && tid < BK) {
-      // raw per-key scales; commit_tile turns them into multipliers (using
-      // them here would wait for the loads)
       const int64_t si = (int64_t)(t.key0 + min(tid, t.n_valid - 1)) * p.n_heads + head;
       st.ks = t.k_scale[si];
       st.vs = t.v_scale[si];
@@ -342,32 +361,33 @@ __device__ __forceinline__ void issue_part(const AttnParams& p, const TileRef& t
   }
 }
 
-template <int D, bool SCALED, int LW>
-__device__ __forceinline__ void issue_tile(const AttnParams& p, const TileRef& t, int head, Stage<D, LW>& st,
-                                           Smem<D>& sm, int kbuf, const LoadPlan<D, LW>& pl) {
+template <int D, int ST, bool SCALED>
+__device__ __forceinline__ void issue_stage(const AttnParams& p, const TileRef& t, int head,
+                                            Stage<D, ST, SCALED>& st, const LoadPlan<D, ST>& pl) {
 #pragma unroll
-  for (int j = 0; j < TileLoad<D, LW>::NPART; ++j) issue_part<D, SCALED, LW>(p, t, head, st, sm, kbuf, pl, j);
+  for (int j = 0; j < Loader<D, ST>::template npart<SCALED>(); ++j)
+    issue_stage_part<D, ST, SCALED>(p, t, head, st, pl, j);
 }
 
 // Finish tile t: register-staged V (and int8 K) into LDS buffers vbuf (kbuf),
 // scaled-path multipliers into slot kbuf.
-template <int D, bool SCALED, int LW>
-__device__ __forceinline__ void commit_tile(const AttnParams& p, const TileRef& t, const Stage<D, LW>& st,
+template <int D, int ST, bool SCALED>
+__device__ __forceinline__ void commit_tile(const AttnParams& p, const TileRef& t, const Stage<D, ST, SCALED>& st,
                                             Smem<D>& sm, int kbuf, int vbuf) {
   using L = Layout<D>;
-  using LD = Loader<D, LW>;
+  using LD = Loader<D, ST>;
   const int tid = threadIdx.x;
   if (!SCALED || !t.is_int8) {
 #pragma unroll
     for (int j = 0; j < LD::VCH; ++j) {
-      const int lin = tid + j * LD::LT;
+      const int lin = tid + j * ST;
       const int row = lin / L::CPR, c = lin % L::CPR;
       *reinterpret_cast<uint4*>(sm.v[vbuf] + row * L::VS + c * 8) = bf16x8_to_f16x8(st.r[j]);
     }
-  } else if (LD::I8_THREADS >= LD::LT || tid < LD::I8_THREADS) {
+  } else if (LD::I8_THREADS >= ST || tid < LD::I8_THREADS) {
 #pragma unroll
     for (int j = 0; j < LD::I8CH; ++j) {
-      const int lin = tid + j * LD::LT;
+      const int lin = tid + j * ST;
       const int row = lin / (D / 16), c16 = lin % (D / 16);
       uint16_t* kr = sm.k[kbuf] + row * L::KS + 16 * c16;
       uint16_t* vr = sm.v[vbuf] + row * L::VS + 16 * c16;
@@ -664,15 +684,15 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   // 16*(g16&1) + 4*(s16&3) inside each 32-column tile
   const int v_lane = (4 * hh + (s16 >> 2)) * L::VS + 16 * (g16 & 1) + 4 * (s16 & 3);
 
-  // Kernels without int8 segments leave all loading and staging to the
-  // leading waves (which otherwise wait at the barrier for the lagging
-  // ones); kernels with int8 segments share it over all waves (the staged
-  // int8 tiles need the registers).
-  constexpr int LW = SCALED ? NW : NW / 2;
-  const bool loader = wave < LW;
-  Stage<D, LW> st;
-  LoadPlan<D, LW> plan;
-  make_plan<D, LW>(plan, p.n_heads * D);
+  constexpr int ST = SCALED ? NT : NT / 2;   // staging threads (see Loader)
+  using LD = Loader<D, ST>;
+  Stage<D, ST, SCALED> st;
+  LoadPlan<D, ST> plan;
+  make_plan<D, ST>(plan, p.n_heads * D);
+  constexpr int NPART = LD::template npart<SCALED>();
+  constexpr int STRIDE = (2 * NKS) / NPART;
+  const bool k_wave = wave < LD::KW;
+  const bool stager = tid < ST;
   // q-block bits of every wave of the workgroup (tile compaction)
   uint32_t wq[NW];
 #pragma unroll
@@ -725,65 +745,139 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     __syncthreads();
     if (total == 0) continue;
 
-    // ---- prologue: first kept tile into K buffer 0 / V buffer 0
-    TileRef tn = tile_ref(p, sm.desc[0]);
-    if (loader) {
-      issue_tile<D, SCALED, LW>(p, tn, head, st, sm, 0, plan);
-      commit_tile<D, SCALED, LW>(p, tn, st, sm, 0, 0);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    // Tile i lives in K buffer i%2 (and scale slot i%2) and V buffer i%3.
-    // During step i the loads of tile i+1 go to K buffer (i+1)%2 and, at the
-    // end of the step, V buffer (i+1)%3, while the leading waves read tile i
-    // and the lagging ones tiles i-1 (V only) and i.
-    f16x8 pb[4];
-    bool pending = false;   // lagging waves: P of the previous tile awaits its P.V
-    int kbuf = 0, vbuf = 0, vprev = NVBUF - 1;
-#pragma unroll 1
-    for (int it = 0; it < total; ++it) {
-      const TileRef t = tn;
-      const bool has_next = it + 1 < total;
-      const int knext = kbuf ^ 1;
-      const int vnext = (vbuf + 1 == NVBUF) ? 0 : vbuf + 1;
-      if (has_next) tn = tile_ref(p, sm.desc[it + 1]);
-      if (lagging && pending) pv_tile<D, PF_PV>(ws, sm.v[vprev], v_lane, pb);
-      pending = false;
-      if ((t.wmask >> wave) & 1) {
-        // The next tile's register loads ride on the score MFMAs; its
-        // direct-to-LDS loads follow the last score MFMA (the compiler waits
-        // for every LDS read in flight after one of those, which would stall
-        // the operand prefetch inside the MFMA sequence).
-        constexpr int KM = TileLoad<D, LW>::KMAX;
-        constexpr int STRIDE = (2 * NKS) / (TileLoad<D, LW>::NPART - KM);
-        qk_softmax<D, SCALED, GENERAL>(
-            p, t, ws, sm.k[kbuf], sm.ksc[kbuf], sm.vsc[kbuf], k_lane, r, hh, my_qb, qb_lo, n_qbt, pb,
-            [&](int i) {
-              if (loader && has_next && i % STRIDE == 0 && KM + i / STRIDE < TileLoad<D, LW>::NPART)
-                issue_part<D, SCALED, LW>(p, tn, head, st, sm, knext, plan, KM + i / STRIDE);
-            },
-            [&]() {
-              if (loader && has_next)
-#pragma unroll
-                for (int j = 0; j < KM; ++j) issue_part<D, SCALED, LW>(p, tn, head, st, sm, knext, plan, j);
-            });
-        if (lagging)
-          pending = true;
-        else
-          pv_tile<D, PF_PV>(ws, sm.v[vbuf], v_lane, pb);
-      } else if (has_next && loader) {
-        issue_tile<D, SCALED, LW>(p, tn, head, st, sm, knext, plan);
+    if constexpr (!SCALED) {
+      // ---- unscaled kernels: the four leading waves move every tile one
+      // step ahead. Tile i lives in K buffer i%2 and V buffer i%3. During
+      // step i the leading waves' V loads of tile i+1 ride on their score
+      // MFMAs and its direct K loads follow the last score MFMA (the compiler
+      // waits for every LDS read in flight after one of those, which inside
+      // the MFMA sequence drained the operand prefetch); its V is converted
+      // and stored at the end of the step. Waves 4..7 run half a tile behind:
+      // they multiply the previous tile's P with V first, then compute the
+      // current tile's scores and softmax.
+      TileRef tn = tile_ref(p, sm.desc[0]);
+      if (stager) {
+        issue_kdma<D, ST>(p, tn, head, sm, 0, plan);
+        issue_stage<D, ST, SCALED>(p, tn, head, st, plan);
+        commit_tile<D, ST, SCALED>(p, tn, st, sm, 0, 0);
       }
-      if (has_next && loader) commit_tile<D, SCALED, LW>(p, tn, st, sm, knext, vnext);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      vprev = vbuf;
-      kbuf = knext;
-      vbuf = vnext;
+      f16x8 pb[4];
+      bool pending = false;   // lagging waves: P of the previous tile awaits its P.V
+      int kbuf = 0, vbuf = 0, vprev = NVBUF - 1;
+#pragma unroll 1
+      for (int it = 0; it < total; ++it) {
+        const TileRef t = tn;
+        const bool has_next = it + 1 < total;
+        const int knext = kbuf ^ 1;
+        const int vnext = (vbuf + 1 == NVBUF) ? 0 : vbuf + 1;
+        if (has_next) tn = tile_ref(p, sm.desc[it + 1]);
+        if (lagging && pending) pv_tile<D, PF_PV>(ws, sm.v[vprev], v_lane, pb);
+        pending = false;
+        if ((t.wmask >> wave) & 1) {
+          qk_softmax<D, SCALED, GENERAL>(
+              p, t, ws, sm.k[kbuf], sm.ksc[kbuf], sm.vsc[kbuf], k_lane, r, hh, my_qb, qb_lo, n_qbt, pb,
+              [&](int i) {
+                if (stager && has_next && i % STRIDE == 0 && i / STRIDE < NPART)
+                  issue_stage_part<D, ST, SCALED>(p, tn, head, st, plan, i / STRIDE);
+              },
+              [&]() {
+                if (stager && has_next) issue_kdma<D, ST>(p, tn, head, sm, knext, plan);
+              });
+          if (lagging)
+            pending = true;
+          else
+            pv_tile<D, PF_PV>(ws, sm.v[vbuf], v_lane, pb);
+        } else if (has_next && stager) {
+          issue_kdma<D, ST>(p, tn, head, sm, knext, plan);
+          issue_stage<D, ST, SCALED>(p, tn, head, st, plan);
+        }
+        if (has_next && stager) commit_tile<D, ST, SCALED>(p, tn, st, sm, knext, vnext);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        vprev = vbuf;
+        kbuf = knext;
+        vbuf = vnext;
+      }
+      // the last tile's V buffer stays untouched until the next pass's barriers
+      if (pending) pv_tile<D, PF_PV>(ws, sm.v[vprev], v_lane, pb);
+    } else {
+      // ---- scaled kernels. Prologue: first kept tile into K buffer 0 / V
+      // buffer 0, the second one's staged loads into registers.
+      TileRef tc = tile_ref(p, sm.desc[0]);
+      if (k_wave && !tc.is_int8) issue_kdma<D, ST>(p, tc, head, sm, 0, plan);
+      issue_stage<D, ST, SCALED>(p, tc, head, st, plan);
+      commit_tile<D, ST, SCALED>(p, tc, st, sm, 0, 0);
+      TileRef tn1 = tc;
+      if (total > 1) {
+        tn1 = tile_ref(p, sm.desc[1]);
+        issue_stage<D, ST, SCALED>(p, tn1, head, st, plan);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+
+      // Tile i lives in K buffer i%2 (and scale slot i%2) and V buffer i%3.
+      // Step i: every wave commits its staged share of tile i+1 (loaded during
+      // step i-1) and loads its share of tile i+2 into the freed registers; the
+      // K waves also issue tile i+1's direct K loads. Waves 0..3 commit first,
+      // then run scores + softmax and P.V of tile i (vector, matrix, vector,
+      // matrix); waves 4..7 first multiply the previous tile's P with V, then
+      // commit, then run scores + softmax of tile i, keeping P for the next
+      // step (matrix, vector, matrix, vector), so on every SIMD the two waves
+      // alternate between the matrix and the vector units.
+      f16x8 pb[4];
+      bool pending = false;   // lagging waves: P of the previous tile awaits its P.V
+      int kbuf = 0, vbuf = 0, vprev = NVBUF - 1;
+#pragma unroll 1
+      for (int it = 0; it < total; ++it) {
+        const TileRef t = tc;
+        const bool has1 = it + 1 < total, has2 = it + 2 < total;
+        const int knext = kbuf ^ 1;
+        const int vnext = (vbuf + 1 == NVBUF) ? 0 : vbuf + 1;
+        TileRef tn2 = tn1;
+        if (has2) tn2 = tile_ref(p, sm.desc[it + 2]);
+        const bool compute = (t.wmask >> wave) & 1;
+        auto ride = [&](int i) {
+          if (has2 && i % STRIDE == 0 && i / STRIDE < NPART)
+            issue_stage_part<D, ST, SCALED>(p, tn2, head, st, plan, i / STRIDE);
+        };
+        auto none = [&]() {};
+        if (!lagging) {
+          if (has1) {
+            if (k_wave && !tn1.is_int8) issue_kdma<D, ST>(p, tn1, head, sm, knext, plan);
+            commit_tile<D, ST, SCALED>(p, tn1, st, sm, knext, vnext);
+          }
+          if (compute) {
+            qk_softmax<D, SCALED, GENERAL>(p, t, ws, sm.k[kbuf], sm.ksc[kbuf], sm.vsc[kbuf], k_lane, r, hh, my_qb,
+                                           qb_lo, n_qbt, pb, ride, none);
+            pv_tile<D, PF_PV>(ws, sm.v[vbuf], v_lane, pb);
+          } else if (has2) {
+            issue_stage<D, ST, SCALED>(p, tn2, head, st, plan);
+          }
+        } else {
+          if (pending) pv_tile<D, PF_PV>(ws, sm.v[vprev], v_lane, pb);
+          pending = false;
+          if (has1) commit_tile<D, ST, SCALED>(p, tn1, st, sm, knext, vnext);
+          if (compute) {
+            qk_softmax<D, SCALED, GENERAL>(p, t, ws, sm.k[kbuf], sm.ksc[kbuf], sm.vsc[kbuf], k_lane, r, hh, my_qb,
+                                           qb_lo, n_qbt, pb, ride, none);
+            pending = true;
+          } else if (has2) {
+            issue_stage<D, ST, SCALED>(p, tn2, head, st, plan);
+          }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        vprev = vbuf;
+        kbuf = knext;
+        vbuf = vnext;
+        tc = tn1;
+        tn1 = tn2;
+      }
+      // the last tile's V buffer stays untouched until the next pass's barriers
+      if (pending) pv_tile<D, PF_PV>(ws, sm.v[vprev], v_lane, pb);
     }
-    // the last tile's V buffer stays untouched until the next pass's barriers
-    if (pending) pv_tile<D, PF_PV>(ws, sm.v[vprev], v_lane, pb);
   }
 
   // ---- finalise
