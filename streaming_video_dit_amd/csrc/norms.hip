@@ -13,10 +13,11 @@
 // owns one row at a time: lane l holds 16-byte chunks l, l + 64, l + 128, ...
 // of it in registers (every load of the row is issued before the first
 // reduction, and each load instruction covers 1 KB of contiguous row), so x
-// is read from HBM once however many passes the statistics take. The arithmetic is fp64 with
-// one correctly rounded fp64 -> bf16 conversion at the end: in fp32, x - mean
-// of a row whose mean is large against its spread loses bits of the small
-// difference; in fp64 every output is within one bf16 ulp of the exact value.
+// is read from HBM once however many passes the statistics take. The
+// arithmetic is fp64 with one correctly rounded fp64 -> bf16 conversion at
+// the end: in fp32, x - mean of a row whose mean is large against its spread
+// loses bits of the small difference; in fp64 every output is within one
+// bf16 ulp of the exact value.
 #include "sdit_internal.h"
 
 #include <algorithm>

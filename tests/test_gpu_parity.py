@@ -239,6 +239,26 @@ def test_attention_small_cases(case):
         assert np.all(out[rows] == 0)
 
 
+# More than 1024 kept 64-key tiles per workgroup: the kept-tile list is built
+# and walked in passes of 1024 candidates (the second pass starts after the
+# first one's last P.V), in the unscaled and the scaled kernel, with a
+# first pass that keeps nothing.
+@pytest.mark.parametrize("case", ["bf16_two_passes", "int8_empty_first_pass"])
+def test_attention_long_cache_several_passes(case):
+    if case == "bf16_two_passes":
+        q, segs, mask = _rand_case(71, 300, 2, 64, [1000, 69000], ["bf16", "bf16"], 128, 64, 0.6)
+    else:
+        q, segs, mask = _rand_case(72, 200, 1, 128, [66000, 500], ["int8", "bf16"], 128, 64, 0.5)
+        mask[:, :1024] = 0
+    bq, bk = 128, 64
+    assert mask.shape[1] * bk > 1024 * 64
+    _say("attention", case, mask.shape)
+    out, lse = run_attn(q, segs, mask, bq, bk)
+    O, LSE = oracle.attention(q, segs, mask, bq, bk)
+    e = assert_attn_close(out, lse, O, LSE, case)
+    _say(f"   max-abs {e[0]:.2e} ({e[2]:.2e} beyond half an ulp), rel-RMS {e[1]:.2e}")
+
+
 def test_attention_custom_softmax_scale():
     q, segs, mask = _rand_case(5, 200, 2, 128, [100, 200], ["bf16", "bf16"], 128, 128)
     out, lse = run_attn(q, segs, mask, 128, 128, softmax_scale=0.03)
