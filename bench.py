@@ -153,28 +153,41 @@ class Step:
             sdit.window_permute(self.out_w, self.out, cfg.T, cfg.Hl, cfg.Wl, H, d, cfg.window, inverse=True)
 
 
+def device_info(torch):
+    """What the peak figure rests on: the device's compute-unit count (one
+    bf16 32x32x16 MFMA per 32 cycles per SIMD, 4 SIMDs per CU, at the
+    published 2.4 GHz peak engine clock)."""
+    pr = torch.cuda.get_device_properties(0)
+    cus = int(pr.multi_processor_count)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "compute_units": cus,
+            "peak_bf16_tflops_from_cus": round(cus * 4 * 32768 / 32 * 2.4e9 / 1e12, 1)}
+
+
 def measure_norms(cfg: W.Config, torch, sdit, steps: int, warmup: int):
     """Average launch time and HBM rate of the two per-token norms on the
     workload's hidden-state shape (algorithmic bytes: x read and y written
     once, 2 + 2 bytes per element, plus the fp32 parameter vectors once)."""
     n, d = cfg.n_q, cfg.n_heads * cfg.head_dim
     inp = W.make_norm_inputs(cfg.seed, n, d, offset=1.0)
-    x = _dev(inp.x, torch)
-    y = torch.empty_like(x)
+    # successive launches cycle through enough input/output sets to exceed the
+    # 256 MB last-level cache, so the figures are HBM rates
+    n_sets = max(2, -(-768 * 2**20 // (4 * n * d)))
+    xs = [_dev(inp.x, torch) for _ in range(n_sets)]
+    ys = [torch.empty_like(xs[0]) for _ in range(n_sets)]
     g, sc, sh = _dev(inp.gamma, torch), _dev(inp.scale, torch), _dev(inp.shift, torch)
     launches = {
-        "rmsnorm": (lambda: sdit.rmsnorm(x, y, g, n, d), 4 * n * d + 4 * d),
-        "layernorm_modulate": (lambda: sdit.layernorm_modulate(x, y, sc, sh, n, d), 4 * n * d + 8 * d),
+        "rmsnorm": (lambda i: sdit.rmsnorm(xs[i], ys[i], g, n, d), 4 * n * d + 4 * d),
+        "layernorm_modulate": (lambda i: sdit.layernorm_modulate(xs[i], ys[i], sc, sh, n, d), 4 * n * d + 8 * d),
     }
-    res = {"shape": [n, d]}
+    res = {"shape": [n, d], "input_sets": n_sets}
     stream = torch.cuda.current_stream()
     for name, (fn, nbytes) in launches.items():
-        for _ in range(warmup):
-            fn()
+        for i in range(warmup):
+            fn(i % n_sets)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for a, b in evs:
+        for i, (a, b) in enumerate(evs):
             a.record(stream)
-            fn()
+            fn(i % n_sets)
             b.record(stream)
         torch.cuda.synchronize()
         us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
@@ -337,10 +350,12 @@ def main():
                    "kept_tiles": int(step.inp.mask.sum()), "mask_tiles": int(step.inp.mask.size),
                    "effective_gflop": round(step.flops / 1e9, 3), "parallelism": "none (1 GPU)"},
         "attn_ms": round(attn_avg, 5),
+        "attn_ms_median": round(float(np.median(attn_ms)), 5),
         "attn_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5), round(float(np.percentile(attn_ms, 90)), 5)],
         "pct_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "pct_bf16_peak_attn": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "deterministic": h1 == h2,
+        "device": device_info(torch),
         "wall_s_timed": round(t_wall, 3),
         "roofline": {"kernel": "attn_fwd_kernel<128>" if cfg.head_dim == 128 else "attn_fwd_kernel<64>",
                      "bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS,
