@@ -296,8 +296,8 @@ __device__ __forceinline__ void make_plan(LoadPlan<D, ST>& pl, int row_stride) {
 // bias, so their probabilities are exactly 0 and any finite data there is
 // harmless.
 template <int D, int ST>
-__device__ __forceinline__ void issue_kdma(const AttnParams& p, const TileRef& t, int head, Smem<D>& sm, int kbuf,
-                                           const LoadPlan<D, ST>& pl) {
+__device__ __forceinline__ void issue_kdma_to(const AttnParams& p, const TileRef& t, int head, uint16_t* kdst,
+                                              const LoadPlan<D, ST>& pl) {
   using L = Layout<D>;
   constexpr int KW = Loader<D, ST>::KW;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -314,9 +314,15 @@ __device__ __forceinline__ void issue_kdma(const AttnParams& p, const TileRef& t
         const int row = lin / L::K_CH, pc = lin % L::K_CH;
         off = min(row, t.n_valid - 1) * row_stride + (pc < L::CPR ? pc : 0) * 8;
       }
-      __builtin_amdgcn_global_load_lds((const void*)(kb + off), (lds_void*)(sm.k[kbuf] + blk * 64 * 8), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(kb + off), (lds_void*)(kdst + blk * 64 * 8), 16, 0, 0);
     }
   }
+}
+
+template <int D, int ST>
+__device__ __forceinline__ void issue_kdma(const AttnParams& p, const TileRef& t, int head, Smem<D>& sm, int kbuf,
+                                           const LoadPlan<D, ST>& pl) {
+  issue_kdma_to<D, ST>(p, t, head, sm.k[kbuf], pl);
 }
 
 // Register-staged loads of tile t, cut into NPART one-instruction parts so
@@ -609,6 +615,25 @@ __device__ __forceinline__ void pv_tile(WaveState<D>& ws, const uint16_t* vl, in
   }
 }
 
+// Scaled kernels, leading waves: the next tile's direct K loads, then scores,
+// softmax and P.V of this tile. The LDS buffers come in as restrict-qualified
+// pointers: the compiler then knows that the K and V reads do not touch the K
+// buffer being filled and does not make them wait for those loads (with one
+// shared buffer object it waited for the whole load before the first score
+// MFMA).
+template <int D, bool SCALED, bool GENERAL, int ST, int PF, typename Ride>
+__device__ __forceinline__ void lead_tile_scaled(const AttnParams& p, const TileRef& t, const TileRef& tn, int head,
+                                                 WaveState<D>& ws, const uint16_t* __restrict__ kcur,
+                                                 const float* __restrict__ ksc, const float* __restrict__ vsc,
+                                                 const uint16_t* __restrict__ vcur, uint16_t* __restrict__ knew,
+                                                 bool dma, const LoadPlan<D, ST>& plan, int k_lane, int v_lane,
+                                                 int r, int hh, int my_qb, int qb_lo, int n_qbt, f16x8 (&pb)[4],
+                                                 Ride&& ride) {
+  if (dma) issue_kdma_to<D, ST>(p, tn, head, knew, plan);
+  qk_softmax<D, SCALED, GENERAL>(p, t, ws, kcur, ksc, vsc, k_lane, r, hh, my_qb, qb_lo, n_qbt, pb, ride, [] {});
+  pv_tile<D, PF>(ws, vcur, v_lane, pb);
+}
+
 // Query-block bits (relative to the workgroup's first q-block) that wave w's
 // 32 rows touch; 0 for a wave whose rows all lie past n_q.
 __device__ __forceinline__ uint32_t wave_qbits(const AttnParams& p, int q_lo, int qb_lo, int w) {
@@ -844,16 +869,15 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         };
         auto none = [&]() {};
         if (!lagging) {
-          if (has1) {
-            if (k_wave && !tn1.is_int8) issue_kdma<D, ST>(p, tn1, head, sm, knext, plan);
-            commit_tile<D, ST, SCALED>(p, tn1, st, sm, knext, vnext);
-          }
+          const bool dma = has1 && k_wave && !tn1.is_int8;
+          if (has1) commit_tile<D, ST, SCALED>(p, tn1, st, sm, knext, vnext);
           if (compute) {
-            qk_softmax<D, SCALED, GENERAL>(p, t, ws, sm.k[kbuf], sm.ksc[kbuf], sm.vsc[kbuf], k_lane, r, hh, my_qb,
-                                           qb_lo, n_qbt, pb, ride, none);
-            pv_tile<D, PF_PV>(ws, sm.v[vbuf], v_lane, pb);
-          } else if (has2) {
-            issue_stage<D, ST, SCALED>(p, tn2, head, st, plan);
+            lead_tile_scaled<D, SCALED, GENERAL, ST, PF_PV>(p, t, tn1, head, ws, sm.k[kbuf], sm.ksc[kbuf],
+                                                            sm.vsc[kbuf], sm.v[vbuf], sm.k[knext], dma, plan,
+                                                            k_lane, v_lane, r, hh, my_qb, qb_lo, n_qbt, pb, ride);
+          } else {
+            if (dma) issue_kdma<D, ST>(p, tn1, head, sm, knext, plan);
+            if (has2) issue_stage<D, ST, SCALED>(p, tn2, head, st, plan);
           }
         } else {
           if (pending) pv_tile<D, PF_PV>(ws, sm.v[vprev], v_lane, pb);
