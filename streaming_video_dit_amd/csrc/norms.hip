@@ -136,7 +136,7 @@ __device__ __forceinline__ uint4 norm_chunk(const uint4& raw, double mean, doubl
       else
         v[h] = v[h] * inv * (double)g[j];
     }
-    o[e] = f64_to_bf16_rne(v[0]) | (f64_to_bf16_rne(v[1]) << 16);
+    o[e] = f64x2_to_bf16x2(v[0], v[1]);
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }

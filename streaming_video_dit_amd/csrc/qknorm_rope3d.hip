@@ -29,6 +29,47 @@ constexpr int kHeadsPerUnit = 4;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// sin and cos of an fp64 angle, to about one ulp (rotation angles are
+// position x frequency, so |x| stays far below 2^20 pi/2). Cody and Waite's
+// argument reduction: k = rint(x * 2/pi) and r = x - k pi/2 with pi/2 split
+// into three doubles; the first two carry 33 significant bits, so k times each
+// is exact for |k| < 2^20, and the third holds the next 53 bits of pi/2
+// (the three together are within 1e-37 of pi/2). Then the Taylor series of
+// sin and cos in r^2 on |r| <= pi/4, to the r^19 and r^18 terms (the first
+// terms left out are below 1e-19 relative), and the quadrant k mod 4 selects
+// +-sin or +-cos. Larger angles fall back to the library routine.
+__device__ __forceinline__ void sincos_f64(double x, double& s, double& c) {
+  constexpr double kTwoOverPi = 0x1.45f306dc9c883p-1;
+  constexpr double kPio2a = 0x1.921fb544p+0;
+  constexpr double kPio2b = 0x1.0b4611a6p-34;
+  constexpr double kPio2c = 0x1.3198a2e037073p-69;
+  if (!(fabs(x) < 0x1p20)) {
+    sincos(x, &s, &c);
+    return;
+  }
+  const double k = rint(x * kTwoOverPi);
+  const double r = fma(-k, kPio2c, fma(-k, kPio2b, fma(-k, kPio2a, x)));
+  const double z = r * r;
+  // Horner in z with coefficients (-1)^n / (2n+1)! and (-1)^n / (2n)!, n = 9..1
+  double ps = -1.0 / 121645100408832000.0;   // -1/19!
+  double pc = -1.0 / 6402373705728000.0;     // -1/18!
+  double fs = 121645100408832000.0, fc = 6402373705728000.0;
+#pragma unroll
+  for (int n = 8; n >= 1; --n) {
+    fs /= (double)((2 * n + 2) * (2 * n + 3));
+    fc /= (double)((2 * n + 1) * (2 * n + 2));
+    const double sign = (n & 1) ? -1.0 : 1.0;
+    ps = fma(ps, z, sign / fs);
+    pc = fma(pc, z, sign / fc);
+  }
+  const double sr = fma(r * z, ps, r);
+  const double cr = fma(z, pc, 1.0);
+  const int q = (int)k & 3;
+  const double s0 = (q & 1) ? cr : sr, c0 = (q & 1) ? sr : cr;
+  s = (q & 2) ? -s0 : s0;
+  c = ((q + 1) & 2) ? -c0 : c0;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
   constexpr int LPR = D / 8;
@@ -76,16 +117,8 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = c0 + 2 * i;           // first column of the pair
-    int pos, j, da;
-    if (c < p.d_t) {
-      pos = pos_t; j = c / 2; da = p.d_t;
-    } else if (c < p.d_t + p.d_h) {
-      pos = pos_h; j = (c - p.d_t) / 2; da = p.d_h;
-    } else {
-      pos = pos_w; j = (c - p.d_t - p.d_h) / 2; da = p.d_w;
-    }
-    const double omega = exp2(-2.0 * (double)j / (double)da * p.log2_theta);
-    sincos((double)pos * omega, &sn[i], &cs[i]);
+    const int pos = c < p.d_t ? pos_t : (c < p.d_t + p.d_h ? pos_h : pos_w);
+    sincos_f64((double)pos * p.omega[c / 2], sn[i], cs[i]);
   }
 
 #pragma unroll
@@ -112,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
       const double y1 = x[2 * e + 1] * inv * (double)g[t][2 * e + 1];
       const double r0 = y0 * cs[e] - y1 * sn[e];
       const double r1 = y0 * sn[e] + y1 * cs[e];
-      o[e] = f64_to_bf16_rne(r0) | (f64_to_bf16_rne(r1) << 16);
+      o[e] = f64x2_to_bf16x2(r0, r1);
     }
     uint16_t* out = t ? p.k_out : p.q_out;
     if (active && hi < nh)

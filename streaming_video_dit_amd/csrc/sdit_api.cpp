@@ -124,7 +124,15 @@ SDIT_API int sdit_qknorm_rope3d(const void* q_in, const void* k_in, void* q_out,
   p.d_t = d_t;
   p.d_h = d_h;
   p.d_w = d_w;
-  p.log2_theta = log2((double)theta);
+  // pair j of an axis of width d_a turns at theta^(-2j/d_a), in column order t | h | w
+  {
+    int c = 0;
+    for (int a = 0; a < 3; ++a) {
+      const int da = a == 0 ? d_t : (a == 1 ? d_h : d_w);
+      for (int j = 0; j < da / 2; ++j) p.omega[c++] = pow((double)theta, -2.0 * j / da);
+    }
+    for (; c < 64; ++c) p.omega[c] = 0.0;
+  }
   p.eps = eps;
   if (p.n_tok == 0) return ok();
   return device_status(sdit::launch_qknorm_rope3d(p, head_dim, (hipStream_t)stream), "qknorm_rope3d");

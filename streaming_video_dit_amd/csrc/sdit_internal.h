@@ -23,6 +23,22 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
   return u >> 16;
 }
 
+// Two fp64 values -> two bf16 packed (a in the low half), correctly rounded.
+// Rounding to fp32 first and then to bf16 (the hardware conversion, round to
+// nearest even) gives the same bf16 as rounding the fp64 value directly
+// unless the fp32 value sits exactly half-way between two bf16 values: any
+// other bf16 rounding boundary lying between the fp64 value and its fp32
+// rounding would itself be an fp32 value closer to the fp64 value. Only that
+// case (about one output in 65536) takes the exact path above.
+__device__ __forceinline__ uint32_t f64x2_to_bf16x2(double a, double b) {
+  const float fa = (float)a, fb = (float)b;
+  if (((__float_as_uint(fa) & 0xFFFFu) == 0x8000u) | ((__float_as_uint(fb) & 0xFFFFu) == 0x8000u))
+    return f64_to_bf16_rne(a) | (f64_to_bf16_rne(b) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)fa, (__bf16)fb};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 
 // ---------------------------------------------------------------- qknorm_rope3d
 struct RopeParams {
@@ -34,7 +50,7 @@ struct RopeParams {
   const float* gamma_k;
   int32_t n_tok, Hl, Wl, t0;
   int32_t n_heads, d_t, d_h, d_w;
-  double log2_theta;   // log2(theta), computed on the host in double
+  double omega[64];    // rotation frequency of pair c/2: theta^(-2j/d_axis), computed on the host
   float eps;
 };
 hipError_t launch_qknorm_rope3d(const RopeParams& p, int head_dim, hipStream_t stream);

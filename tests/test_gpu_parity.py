@@ -120,6 +120,22 @@ def test_qknorm_rope3d_in_place_equals_out_of_place():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+# Far frame positions: rotation angles up to ~7e4 rad go through the
+# kernel's own argument reduction, and past 2^20 rad through the fallback.
+@pytest.mark.parametrize("t0", [70000, 1 << 21])
+def test_qknorm_rope3d_far_positions(t0):
+    geo = (2, 3, 5, t0, W.rope_split(128))
+    n, H, d = 2 * 3 * 5, 4, 128
+    q = W.normal_bf16(32, 0, (n, H, d))
+    k = W.normal_bf16(32, 1, (n, H, d))
+    gq = W.uniform_f32(32, 2, (d,), 0.5, 1.5)
+    gk = W.uniform_f32(32, 3, (d,), 0.5, 1.5)
+    _say("qknorm_rope3d t0", t0)
+    a, b = _gpu_rope(geo, q, k, gq, gk)
+    _check_rope(a, q, gq, geo)
+    _check_rope(b, k, gk, geo)
+
+
 @pytest.mark.parametrize("split,d", [((64, 0, 0), 64), ((0, 0, 64), 64), ((20, 24, 20), 64), ((0, 128, 0), 128)])
 def test_qknorm_rope3d_other_splits(split, d):
     geo = (2, 3, 5, 7, split)
