@@ -47,7 +47,7 @@ extern "C" {
 typedef enum sdit_status {
   SDIT_OK = 0,
   SDIT_ERR_INVALID = 1,     /* bad argument; nothing was launched            */
-  SDIT_ERR_UNSUPPORTED = 2, /* valid request this build/device cannot run    */
+  SDIT_ERR_UNSUPPORTED = 2, /* valid request this library/device cannot run  */
   SDIT_ERR_DEVICE = 3       /* the HIP runtime reported an error at launch   */
 } sdit_status;
 
