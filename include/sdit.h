@@ -30,6 +30,10 @@
  *     4-byte aligned.
  *   - Inputs must be finite. Only tiles that the block mask skips may hold
  *     non-finite values (they are never read).
+ *   - No one tensor may hold more than 2^40 elements (tokens x heads x
+ *     head_dim): larger requests return SDIT_ERR_INVALID. Size products are
+ *     formed without integer overflow, so extreme 32-bit arguments are
+ *     rejected, never wrapped into a small size.
  */
 #ifndef SDIT_H
 #define SDIT_H
@@ -200,7 +204,9 @@ int sdit_attn_merge(const float* const* o_parts, const float* const* lse_parts, 
  *   x, y       bf16 [T*Hl*Wl][n_heads][head_dim]; must not overlap
  *   inverse    0: x raster -> y window-major; 1: x window-major -> y raster
  *   window     2, 4, 8 or 16; Hl and Wl multiples of it
- *   head_dim   64 or 128; T, Hl or Wl == 0 is a no-op. */
+ *   head_dim   64 or 128; T, Hl or Wl == 0 is a no-op
+ *   T*Hl*Wl    below 2^30; n_heads * head_dim at most 2^24 (else
+ *              SDIT_ERR_UNSUPPORTED). */
 int sdit_window_permute(const void* x, void* y, int32_t T, int32_t Hl, int32_t Wl,
                         int32_t n_heads, int32_t head_dim, int32_t window, int32_t inverse, void* stream);
 

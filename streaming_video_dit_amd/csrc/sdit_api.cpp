@@ -45,7 +45,15 @@ int device_status(hipError_t e, const char* what) {
   return fail(SDIT_ERR_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
 }
 
-int ceil_div(int a, int b) { return (a + b - 1) / b; }
+// a >= 0, b > 0; no intermediate a + b - 1 that could pass INT32_MAX
+int ceil_div(int a, int b) { return a / b + (a % b != 0); }
+
+// a * b for a, b >= 0, saturated at INT64_MAX: size checks compare the
+// result with limits far below that, so a saturated product is rejected
+int64_t mul_sat(int64_t a, int64_t b) { return (a != 0 && b > INT64_MAX / a) ? INT64_MAX : a * b; }
+
+// largest element count (n_tok * n_heads * head_dim) of any one tensor
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
 
 bool valid_block(int b) { return b == 16 || b == 32 || b == 64 || b == 128; }
 
@@ -82,8 +90,9 @@ SDIT_API int sdit_validate_qknorm_rope3d_args(const void* q_in, const void* k_in
                 d_w, head_dim);
   if (!(theta > 0.f) || !isfinite(theta)) return fail(SDIT_ERR_INVALID, "qknorm_rope3d: theta must be > 0");
   if (!(eps >= 0.f) || !isfinite(eps)) return fail(SDIT_ERR_INVALID, "qknorm_rope3d: eps must be >= 0");
-  const int64_t n_tok = (int64_t)T * Hl * Wl;
+  const int64_t n_tok = mul_sat(mul_sat(T, Hl), Wl);
   if (n_tok > INT32_MAX) return fail(SDIT_ERR_INVALID, "qknorm_rope3d: too many tokens");
+  if (n_tok * n_heads > kMaxElems / head_dim) return fail(SDIT_ERR_INVALID, "qknorm_rope3d: q/k too large");
   if ((int64_t)t0 + T > (1 << 24)) return fail(SDIT_ERR_INVALID, "qknorm_rope3d: t positions too large");
   if (n_tok == 0) return ok();
   const void* ptrs[4] = {q_in, k_in, q_out, k_out};
@@ -116,7 +125,7 @@ SDIT_API int sdit_qknorm_rope3d(const void* q_in, const void* k_in, void* q_out,
   p.k_out = (uint16_t*)k_out;
   p.gamma_q = gamma_q;
   p.gamma_k = gamma_k;
-  p.n_tok = T * Hl * Wl;
+  p.n_tok = (int32_t)((int64_t)T * Hl * Wl);   // validated: at most INT32_MAX
   p.Hl = Hl;
   p.Wl = Wl;
   p.t0 = t0;
@@ -151,6 +160,7 @@ SDIT_API int sdit_validate_kv_quant_args(const void* x, const int8_t* codes, con
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4))
     return fail(SDIT_ERR_INVALID, "kv_quant_int8: x/codes must be 16-byte and scales 4-byte aligned");
   const int64_t rows = (int64_t)n_tok * n_heads;
+  if (rows > kMaxElems / head_dim) return fail(SDIT_ERR_INVALID, "kv_quant_int8: x too large");
   if (overlap(codes, rows * head_dim, x, rows * head_dim * 2) || overlap(scales, rows * 4, x, rows * head_dim * 2) ||
       overlap(scales, rows * 4, codes, rows * head_dim))
     return fail(SDIT_ERR_INVALID, "kv_quant_int8: buffers overlap");
@@ -193,7 +203,7 @@ int fill_attn_params(const void* q, int32_t n_q, const sdit_kv_segment* segs, in
     return fail(SDIT_ERR_INVALID, "attn_fwd: n_segs %d not in [1, %d]", n_segs, SDIT_MAX_SEGMENTS);
   if (segs == nullptr) return fail(SDIT_ERR_INVALID, "attn_fwd: segs is NULL");
   if (!isfinite(softmax_scale)) return fail(SDIT_ERR_INVALID, "attn_fwd: softmax_scale not finite");
-  if ((int64_t)n_q * n_heads * head_dim > ((int64_t)1 << 40)) return fail(SDIT_ERR_INVALID, "attn_fwd: q too large");
+  if ((int64_t)n_q * n_heads > kMaxElems / head_dim) return fail(SDIT_ERR_INVALID, "attn_fwd: q too large");
   int64_t tiles = 0, kbs = 0;
   for (int s = 0; s < n_segs; ++s) {
     const sdit_kv_segment& sg = segs[s];
@@ -214,7 +224,7 @@ int fill_attn_params(const void* q, int32_t n_q, const sdit_kv_segment* segs, in
       if (overlap(out, out_bytes, sg.k, seg_bytes) || overlap(out, out_bytes, sg.v, seg_bytes))
         return fail(SDIT_ERR_INVALID, "attn_fwd: out overlaps segment %d", s);
     }
-    tiles += (sg.len + sdit::kAttnBK - 1) / sdit::kAttnBK;
+    tiles += ceil_div(sg.len, sdit::kAttnBK);
     kbs += ceil_div(sg.len, block_k);
   }
   if (tiles > (1 << 24))
@@ -315,7 +325,7 @@ int fill_merge_params(const float* const* o_parts, const float* const* lse_parts
   if (n_parts < 1 || n_parts > SDIT_MAX_MERGE_PARTS)
     return fail(SDIT_ERR_INVALID, "attn_merge: n_parts %d not in [1, %d]", n_parts, SDIT_MAX_MERGE_PARTS);
   if (o_parts == nullptr || lse_parts == nullptr) return fail(SDIT_ERR_INVALID, "attn_merge: part arrays are NULL");
-  if ((int64_t)n_q * n_heads * head_dim > ((int64_t)1 << 40)) return fail(SDIT_ERR_INVALID, "attn_merge: too large");
+  if ((int64_t)n_q * n_heads > kMaxElems / head_dim) return fail(SDIT_ERR_INVALID, "attn_merge: too large");
   const int64_t obytes = (int64_t)n_q * n_heads * head_dim * 2;
   const int64_t fbytes = 2 * obytes, lbytes = (int64_t)n_q * n_heads * 4;
   if (n_q > 0) {
@@ -385,8 +395,12 @@ int fill_permute_params(const void* x, const void* y, int32_t T, int32_t Hl, int
     return fail(SDIT_ERR_INVALID, "window_permute: frame %d x %d is not whole %d x %d windows", Hl, Wl, window,
                 window);
   if (inverse != 0 && inverse != 1) return fail(SDIT_ERR_INVALID, "window_permute: inverse must be 0 or 1");
-  const int64_t n_tok = (int64_t)T * Hl * Wl;
+  // a workgroup walks 8 rows of n_heads * head_dim / 8 16-byte chunks with 32-bit indices
+  if ((int64_t)n_heads * head_dim > (1 << 24))
+    return fail(SDIT_ERR_UNSUPPORTED, "window_permute: row of %d heads x %d too wide", n_heads, head_dim);
+  const int64_t n_tok = mul_sat(mul_sat(T, Hl), Wl);
   if (n_tok > INT32_MAX / 2) return fail(SDIT_ERR_INVALID, "window_permute: too many tokens");
+  if (n_tok * n_heads > kMaxElems / head_dim) return fail(SDIT_ERR_INVALID, "window_permute: x too large");
   const int64_t bytes = n_tok * n_heads * head_dim * 2;
   if (n_tok > 0) {
     if (x == nullptr || y == nullptr || !aligned(x, 16) || !aligned(y, 16))

@@ -220,6 +220,39 @@ def test_norm_validation():
     assert "layernorm_modulate" in (ln(dim=12), sdit.last_error())[1]
 
 
+def test_extreme_sizes_are_rejected_not_wrapped():
+    """Sizes near the int32 limits: each product of dimensions is formed
+    without overflow and compared with its limit, so a huge request is
+    rejected instead of wrapping into a small, valid-looking size."""
+    I32 = 2**31 - 1
+    far = [A16 + (i << 44) for i in range(1, 8)]        # disjoint fake buffers, 16 TB apart
+    INV, UNS, OK = sdit.SDIT_ERR_INVALID, sdit.SDIT_ERR_UNSUPPORTED, sdit.SDIT_OK
+
+    def qk(T, Hl, Wl, n_heads):
+        return sdit.validate_qknorm_rope3d_args(A16, A16, far[0], far[1], far[2], far[3], T, Hl, Wl, 0,
+                                                n_heads, 128, 44, 42, 42)
+    assert qk(I32, I32, I32, 1) == INV                   # T * Hl * Wl past 2^63
+    assert qk(65536, 65536, 0, 12) == OK                 # T * Hl alone past int32, but no tokens
+    assert qk(1 << 15, 1 << 15, 1, 12) == INV            # 2^30 tokens x 12 heads x 128 > 2^40 elements
+    assert qk(16, 16, 16, I32) == INV                    # head count that would wrap the byte size
+    assert sdit.validate_kv_quant_args(A16, far[0], far[1], I32, I32, 128) == INV
+    assert sdit.validate_kv_quant_args(A16, far[0], far[1], 1 << 20, 1 << 13, 128) == OK   # exactly 2^40
+    assert sdit.validate_kv_quant_args(A16, far[0], far[1], 1 << 20, (1 << 13) + 1, 128) == INV
+
+    def wp(T, Hl, Wl, n_heads):
+        return sdit.validate_window_permute_args(A16, far[0], T, Hl, Wl, n_heads, 128, 8, False)
+    assert wp(I32, 1 << 24, 1 << 24, 1) == INV           # T * Hl * Wl past 2^63
+    assert wp(1, 64, 64, I32) == UNS                     # row of n_heads * head_dim wider than 2^24
+    assert wp(1 << 14, 128, 128, 4096) == INV            # 2^28 tokens x 2^19 per token > 2^40 elements
+    assert wp(0, 1 << 20, 1 << 20, 12) == OK
+    assert sdit.validate_attn_merge_args([far[0]], [far[1]], I32, I32, 128, far[2], far[3]) == INV
+    assert sdit.validate_attn_merge_args([far[0]], [far[1]], 1 << 24, 1 << 9, 128, far[2], far[3]) == OK
+
+    huge = sdit.make_segments([dict(k=A16, v=A16, len=I32)])
+    assert sdit.validate_attn_args(far[0], 4096, huge, far[1], 128, 128, 12, 128, far[2], None) == UNS
+    assert sdit.validate_attn_args(far[0], I32, huge, far[1], 16, 16, 1 << 16, 128, far[2], None) == INV
+
+
 def test_error_message_is_per_call():
     sdit.validate_kv_quant_args(A16, A16 + 8, A16 + 32 * MB, 100, 12, 128)
     assert sdit.last_error() != ""
