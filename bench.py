@@ -5,7 +5,13 @@ One step = one layer-chunk of the hot path on seeded synthetic inputs already
 resident in HBM:
     qknorm_rope3d(chunk q, k)            (skipped by the self-attention SR workload)
     kv_quant_int8(chunk K), (chunk V)    (int8-cache workload: the steady-state cache write)
-    attn_fwd(q, [cache segments..., current chunk])
+    attn_fwd_balanced(q, [cache segments..., current chunk])
+
+The attention call is sdit_attn_fwd_balanced with the library's own plan:
+on each XCD the work units of the grid's last partial wave are cut at one
+key tile into head and tail pieces, and a second kernel merges the two
+pieces (both launches are inside the timed attention). --launch plain times
+sdit_attn_fwd instead (one workgroup per unit, no cut, no merge).
 
 With --kv-parts N (N > 1) the attention is the split-KV form instead: the
 segments are cut into N groups of consecutive segments, attn_fwd_partial
@@ -22,6 +28,7 @@ Prints ONE JSON line. ``value`` is effective attention TFLOP/s of the whole
 step (kept-tile FLOPs 4*d*H*sum rows*cols / step time); ``ms_per_step`` is
 the ms/layer/chunk. ``roofline`` reports the attention kernel alone, timed
 with HIP events around each launch on the stream it runs on.
+The attention time covers both launches of the balanced call.
 ``cpu_baseline`` times the fp64 oracle on the host (heads processed one by
 one until about 10 s have elapsed, scaled to TFLOP/s).
 """
@@ -56,7 +63,8 @@ def _dev(a, torch):
 class Step:
     """Device buffers and the launch sequence of one layer-chunk."""
 
-    def __init__(self, cfg: W.Config, torch, sdit, kv_parts: int = 1):
+    def __init__(self, cfg: W.Config, torch, sdit, kv_parts: int = 1, launch: str = "balanced",
+                 split_tile: int = -1):
         self.cfg, self.torch, self.sdit = cfg, torch, sdit
         inp = W.make_inputs(cfg)
         self.inp = inp
@@ -112,6 +120,14 @@ class Step:
                 self.groups.append((sdit.make_segments(segs[a:b]), b - a, _dev(cols, torch), o, ls))
             self.merge_bytes = (kv_parts * (4 * d + 4) + 2 * d + 4) * n * H
         self.q_attn = self.q_w if cfg.window else (self.q if cfg.rope else self.q_in)
+        self.launch = launch
+        self.n_tiles = sum(-(-int(sg["len"]) // 64) for sg in segs)
+        self.plan = (0, cfg.n_heads * -(-n // 256))
+        if launch == "balanced":
+            self.ws = torch.empty((sdit.attn_workspace_bytes(d),), dtype=torch.uint8, device="cuda")
+            cus = torch.cuda.get_device_properties(0).multi_processor_count
+            self.split_tile = split_tile
+            self.plan = sdit.attn_balanced_plan(n, H, self.n_tiles, cus, split_tile)
         self.quant_chunk = any(cfg.seg_int8)
         if self.quant_chunk:
             self.ck = torch.empty((n, H, d), dtype=torch.int8, device="cuda")
@@ -145,6 +161,9 @@ class Step:
             if ev_merge is not None:
                 ev_merge.record()
             sdit.attn_merge([g[3] for g in self.groups], [g[4] for g in self.groups], n, H, d, out, self.lse)
+        elif self.launch == "balanced":
+            sdit.attn_fwd_balanced(self.q_attn, n, self.segs, self.mask, cfg.block, cfg.block, H, d, out, self.ws,
+                                   self.lse, split_tile=self.split_tile)
         else:
             sdit.attn_fwd(self.q_attn, n, self.segs, self.mask, cfg.block, cfg.block, H, d, out, self.lse)
         if ev_after is not None:
@@ -198,17 +217,26 @@ def measure_norms(cfg: W.Config, torch, sdit, steps: int, warmup: int):
     return res
 
 
+def attn_src_hash() -> str:
+    """sha256 prefix of the attention kernels' sources (attn_fwd.hip, then
+    attn_merge.hip, which holds the merge of a balanced launch)."""
+    h = hashlib.sha256()
+    for f in ("attn_fwd.hip", "attn_merge.hip"):
+        h.update(open(os.path.join(ROOT, "streaming_video_dit_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs summarised under profiles/ (calibrated against a plain copy). The
-    figures belong to one version of the kernel source: once attn_fwd.hip has
-    changed they no longer describe it and None is returned."""
+    """HBM bytes per attention call (the attention kernel, plus the merge
+    kernel when the balanced plan cuts) from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs summarised under profiles/ (calibrated against a plain
+    copy). The figures belong to one version of the kernel sources: once
+    they have changed they no longer describe them and None is returned."""
     f = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
     if not os.path.exists(f):
         return None
     t = json.load(open(f))
-    src = os.path.join(ROOT, "streaming_video_dit_amd", "csrc", "attn_fwd.hip")
-    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != t.get("attn_fwd_src_sha256_16"):
+    if attn_src_hash() != t.get("attn_src_sha256_16"):
         return None
     w = t["workloads"].get(workload)
     return None if w is None else int(w["fetch_bytes"] + w["write_bytes"])
@@ -274,6 +302,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--kv-parts", type=int, default=1,
                     help="split-KV form: attention over this many groups of segments, then the merge")
+    ap.add_argument("--launch", choices=["balanced", "plain"], default="balanced",
+                    help="attention entry point: sdit_attn_fwd_balanced (library plan) or sdit_attn_fwd")
+    ap.add_argument("--split-tile", type=int, default=-1,
+                    help="balanced launch: key tile of the cut (-1: the library's plan, 0: none)")
     ap.add_argument("--with-norms", action="store_true",
                     help="also time RMSNorm and LayerNorm + modulate on the workload's hidden-state shape")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -303,7 +335,7 @@ def main():
         return
 
     cfg = W.CONFIGS[args.workload]
-    step = Step(cfg, torch, sdit, args.kv_parts)
+    step = Step(cfg, torch, sdit, args.kv_parts, args.launch, args.split_tile)
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -348,7 +380,9 @@ def main():
                    "head_dim": cfg.head_dim, "n_q": cfg.n_q, "segments": cfg.seg_lens,
                    "int8_segments": cfg.seg_int8, "block": cfg.block,
                    "kept_tiles": int(step.inp.mask.sum()), "mask_tiles": int(step.inp.mask.size),
-                   "effective_gflop": round(step.flops / 1e9, 3), "parallelism": "none (1 GPU)"},
+                   "effective_gflop": round(step.flops / 1e9, 3), "parallelism": "none (1 GPU)",
+                   "launch": args.launch if args.kv_parts == 1 else "split-kv",
+                   "key_tiles": step.n_tiles, "cut_at_tile": step.plan[0], "attn_workgroups": step.plan[1]},
         "attn_ms": round(attn_avg, 5),
         "attn_ms_median": round(float(np.median(attn_ms)), 5),
         "attn_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5), round(float(np.percentile(attn_ms, 90)), 5)],
@@ -357,7 +391,8 @@ def main():
         "deterministic": h1 == h2,
         "device": device_info(torch),
         "wall_s_timed": round(t_wall, 3),
-        "roofline": {"kernel": "attn_fwd_kernel<128>" if cfg.head_dim == 128 else "attn_fwd_kernel<64>",
+        "roofline": {"kernel": (f"attn_fwd_kernel<{cfg.head_dim}>"
+                               + (f" + attn_split_merge_kernel<{cfg.head_dim}>" if step.plan[0] > 0 else "")),
                      "bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(cfg.name)},

@@ -159,6 +159,42 @@ int sdit_attn_fwd(const void* q, int32_t n_q,
                   int32_t n_heads, int32_t head_dim, float softmax_scale,
                   void* out, float* lse, void* stream);
 
+/* sdit_attn_fwd with the grid's last partial wave balanced over the CUs.
+ * Same computation and arguments as sdit_attn_fwd (so the same passages),
+ * plus a caller-owned device workspace. Work units (head, 256 query rows)
+ * are dealt to the 8 XCDs in contiguous ranges; on an XCD whose units do not
+ * fill whole waves of its CUs, the units of the last partial wave are cut at
+ * one key tile into a head piece and a tail piece, which run on the CUs
+ * that the partial wave would leave idle, and a second kernel combines the
+ * two pieces' normalised fp32 partials with the log-sum-exp identity of
+ * sdit_attn_merge (so outputs may differ from sdit_attn_fwd in the last
+ * bf16 bit). Head pieces all start at the first key tile, so the units on an
+ * XCD still walk the keys together and share its L2.
+ *   workspace        device memory, 16-byte aligned, at least
+ *                    SDIT_ATTN_WORKSPACE_BYTES(head_dim) bytes, not
+ *                    overlapping any argument; its contents on entry do not
+ *                    matter and are undefined after the call. Calls that
+ *                    share a workspace must be ordered on one stream.
+ *   workspace_bytes  its size
+ *   split_tile       -1: the library plans the cut from the shape and the
+ *                    device's CU count (no cut when it would not pay);
+ *                    0: never cut (then this is sdit_attn_fwd);
+ *                    t >= 1: cut at key tile t (64-key tiles counted over the
+ *                    concatenated segments, t < their total), for tests. */
+#define SDIT_ATTN_WORKSPACE_BYTES(head_dim) ((int64_t)8 * 31 * 2 * 256 * ((head_dim) + 1) * 4)
+/* The cut sdit_attn_fwd_balanced makes (host only, nothing launched): for
+ * n_q queries, n_heads heads and n_tiles 64-key tiles over the segments on
+ * a device of n_cus CUs, *tile receives the key tile of the cut (0: none)
+ * and *grid the workgroups of the attention launch. split_tile as above. */
+int sdit_attn_balanced_plan(int32_t n_q, int32_t n_heads, int32_t n_tiles, int32_t n_cus,
+                            int32_t split_tile, int32_t* tile, int32_t* grid);
+int sdit_attn_fwd_balanced(const void* q, int32_t n_q,
+                           const sdit_kv_segment* segs, int32_t n_segs,
+                           const uint8_t* block_mask, int32_t block_q, int32_t block_k,
+                           int32_t n_heads, int32_t head_dim, float softmax_scale,
+                           void* out, float* lse, void* workspace, int64_t workspace_bytes,
+                           int32_t split_tile, void* stream);
+
 /* Partial attention for a split of the keys (split-KV): the computation of
  * sdit_attn_fwd over the given segments, with O written normalised in fp32
  * so that results over disjoint key sets combine without another rounding
@@ -247,6 +283,12 @@ int sdit_validate_attn_args(const void* q, int32_t n_q,
                             const uint8_t* block_mask, int32_t block_q, int32_t block_k,
                             int32_t n_heads, int32_t head_dim, float softmax_scale,
                             const void* out, const float* lse);
+int sdit_validate_attn_balanced_args(const void* q, int32_t n_q,
+                                     const sdit_kv_segment* segs, int32_t n_segs,
+                                     const uint8_t* block_mask, int32_t block_q, int32_t block_k,
+                                     int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                     const void* out, const float* lse, const void* workspace,
+                                     int64_t workspace_bytes, int32_t split_tile);
 int sdit_validate_attn_partial_args(const void* q, int32_t n_q,
                                     const sdit_kv_segment* segs, int32_t n_segs,
                                     const uint8_t* block_mask, int32_t block_q, int32_t block_k,

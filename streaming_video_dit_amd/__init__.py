@@ -55,12 +55,16 @@ def lib() -> ctypes.CDLL:
                                           _i32, _f32, _vp, _vp]
     L.sdit_attn_fwd_partial.argtypes = L.sdit_attn_fwd.argtypes
     L.sdit_validate_attn_partial_args.argtypes = L.sdit_validate_attn_args.argtypes
+    _i64 = ctypes.c_int64
+    L.sdit_attn_fwd_balanced.argtypes = L.sdit_attn_fwd.argtypes[:-1] + [_vp, _i64, _i32, _vp]
+    L.sdit_validate_attn_balanced_args.argtypes = L.sdit_validate_attn_args.argtypes + [_vp, _i64, _i32]
+    _pi32 = ctypes.POINTER(ctypes.c_int32)
+    L.sdit_attn_balanced_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _pi32, _pi32]
     _pp = ctypes.POINTER(ctypes.c_void_p)
     L.sdit_attn_merge.argtypes = [_pp, _pp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
     L.sdit_validate_attn_merge_args.argtypes = [_pp, _pp, _i32, _i32, _i32, _i32, _vp, _vp]
     L.sdit_window_permute.argtypes = [_vp, _vp] + [_i32] * 7 + [_vp]
     L.sdit_validate_window_permute_args.argtypes = [_vp, _vp] + [_i32] * 7
-    _i64 = ctypes.c_int64
     L.sdit_rmsnorm.argtypes = [_vp, _vp, _vp, _i64, _i32, _f32, _vp]
     L.sdit_validate_rmsnorm_args.argtypes = [_vp, _vp, _vp, _i64, _i32, _f32]
     L.sdit_layernorm_modulate.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _f32, _vp]
@@ -70,7 +74,8 @@ def lib() -> ctypes.CDLL:
               "sdit_qknorm_rope3d", "sdit_validate_qknorm_rope3d_args", "sdit_kv_quant_int8",
               "sdit_validate_kv_quant_args", "sdit_attn_fwd", "sdit_validate_attn_args",
               "sdit_attn_fwd_partial", "sdit_validate_attn_partial_args", "sdit_attn_merge",
-              "sdit_validate_attn_merge_args"):
+              "sdit_validate_attn_merge_args", "sdit_attn_fwd_balanced", "sdit_validate_attn_balanced_args",
+              "sdit_attn_balanced_plan"):
         getattr(L, n).restype = ctypes.c_int
     if L.sdit_abi_version() != ABI_VERSION:
         raise ImportError(f"libsdit.so ABI {L.sdit_abi_version()} != binding ABI {ABI_VERSION}")
@@ -177,6 +182,40 @@ def attn_fwd(q, n_q: int, segs, block_mask, block_q: int, block_k: int, n_heads:
     n = len(segs)
     _check(lib().sdit_attn_fwd(_ptr(q), n_q, arr, n, _ptr(block_mask), block_q, block_k, n_heads, head_dim,
                               softmax_scale, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def attn_workspace_bytes(head_dim: int) -> int:
+    """SDIT_ATTN_WORKSPACE_BYTES(head_dim): workspace size of attn_fwd_balanced."""
+    return 8 * 31 * 2 * 256 * (head_dim + 1) * 4
+
+
+def attn_fwd_balanced(q, n_q: int, segs, block_mask, block_q: int, block_k: int, n_heads: int, head_dim: int,
+                      out, workspace, lse=None, softmax_scale: float = 0.0, split_tile: int = -1,
+                      workspace_bytes=None, stream=None) -> None:
+    """sdit_attn_fwd_balanced: ``workspace`` is device memory of at least
+    attn_workspace_bytes(head_dim) bytes (its size is taken from the tensor
+    unless ``workspace_bytes`` is given)."""
+    arr = segs if isinstance(segs, ctypes.Array) else make_segments(segs)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().sdit_attn_fwd_balanced(_ptr(q), n_q, arr, len(segs), _ptr(block_mask), block_q, block_k, n_heads,
+                                       head_dim, softmax_scale, _ptr(out), _ptr(lse), _ptr(workspace),
+                                       workspace_bytes, split_tile, _stream(stream)))
+
+
+def attn_balanced_plan(n_q: int, n_heads: int, n_tiles: int, n_cus: int, split_tile: int = -1):
+    """sdit_attn_balanced_plan: (key tile of the cut or 0, workgroups of the launch)."""
+    t, g = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().sdit_attn_balanced_plan(n_q, n_heads, n_tiles, n_cus, split_tile, ctypes.byref(t), ctypes.byref(g)))
+    return t.value, g.value
+
+
+def validate_attn_balanced_args(q, n_q, segs, block_mask, block_q, block_k, n_heads, head_dim, out, lse,
+                                workspace, workspace_bytes, split_tile=-1, softmax_scale: float = 0.0) -> int:
+    arr = segs if isinstance(segs, ctypes.Array) else make_segments(segs)
+    return lib().sdit_validate_attn_balanced_args(_ptr(q), n_q, arr, len(segs), _ptr(block_mask), block_q, block_k,
+                                                 n_heads, head_dim, softmax_scale, _ptr(out), _ptr(lse),
+                                                 _ptr(workspace), workspace_bytes, split_tile)
 
 
 def attn_fwd_partial(q, n_q: int, segs, block_mask, block_q: int, block_k: int, n_heads: int, head_dim: int,

@@ -84,6 +84,13 @@
 //    fp16 P the MFMA multiplies.
 //  * Grid is remapped so consecutive (head, q-tile) work items land on the
 //    same XCD and share its L2 for K/V.
+//  * Balanced launches (sdit_attn_fwd_balanced): on an XCD whose units leave
+//    a partial last wave, those units run as head pieces over the candidate
+//    tiles before a cut and tail pieces over the rest, on the CUs the partial
+//    wave would leave idle; both write normalised fp32 O and LSE to
+//    workspace slots, merged afterwards by attn_split_merge_kernel. The head
+//    pieces all start at the first key tile, so the XCD's units still walk
+//    the keys together.
 #include "sdit_internal.h"
 
 namespace sdit {
@@ -110,7 +117,7 @@ constexpr float MASK_BIAS = -1.0e30f; // added to scores of keys that must not c
 // biased key stays below it because every score multiplier is >= KSC_MIN.
 constexpr float MASKED_MAX = -1.0e15f;
 constexpr float KSC_MIN = 0x1p-40f;   // floor of the per-key score multiplier
-constexpr int NXCD = 8;
+constexpr int NXCD = kNumXcd;
 static_assert(BQ == NW * 32, "one wave per 32 query rows");
 
 template <int D>
@@ -652,11 +659,24 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   constexpr int NDT = D / 32;
   constexpr int PF_PV = SCALED ? 2 : 4;
 
-  // ---- XCD-aware work mapping: consecutive items on one XCD
-  const int G = gridDim.x, b = blockIdx.x;
-  const int xcd = b % NXCD, local = b / NXCD;
-  const int q8 = G / NXCD, r8 = G % NXCD;
-  const int item = (xcd < r8) ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
+  // ---- XCD-aware work mapping: each XCD takes a contiguous range of work
+  // units (head, query tile), so the units on one XCD share its L2 for K/V.
+  // Balanced launches: the XCD's last r units run as head pieces (candidate
+  // tiles [0, split_tile)) and their tail pieces follow as workgroups
+  // n .. n + r - 1 of the XCD, on the CUs that the head pieces leave free.
+  const int xcd = blockIdx.x % NXCD, local = blockIdx.x / NXCD;
+  const XcdUnits xu = xcd_units(p.n_qt * p.n_heads, xcd, p.cu_per_xcd, p.split_tile > 0);
+  int item = xu.u0 + local, c_lo = 0, c_hi = p.n_tiles, slot = -1;
+  if (local >= xu.n) {
+    const int j = local - xu.n;
+    if (j >= xu.r) return;   // padding of the grid
+    item = xu.u0 + xu.n - xu.r + j;
+    slot = (xcd * p.split_rmax + j) * 2 + 1;
+    c_lo = p.split_tile;
+  } else if (local >= xu.n - xu.r) {
+    slot = (xcd * p.split_rmax + local - (xu.n - xu.r)) * 2;
+    c_hi = p.split_tile;
+  }
   const int head = item / p.n_qt;
   const int qt = item % p.n_qt;
 
@@ -724,10 +744,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   for (int w = 0; w < NW; ++w) wq[w] = wave_qbits(p, q_lo, qb_lo, w);
 
 #pragma unroll 1
-  for (int cbase = 0; cbase < p.n_tiles; cbase += LIST_CAP) {
+  for (int cbase = c_lo; cbase < c_hi; cbase += LIST_CAP) {
     // ---- compact the kept tiles of this pass into sm.list (order preserved),
     // with the set of waves that have a kept (q-block, k-block) pair in each
-    const int ncand = min(LIST_CAP, p.n_tiles - cbase);
+    const int ncand = min(LIST_CAP, c_hi - cbase);
     uint32_t wmk[2];
     TileInfo ti[2];
 #pragma unroll
@@ -908,9 +928,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   const float l_tot = swap_halves_sum(ws.l_run);
   const bool any = ws.seen && l_tot > 0.f;
   const float inv = any ? 1.0f / l_tot : 0.f;
-  if (q_ok && p.out_f32 != nullptr) {
-    // partial form: normalised O in fp32, merged later without another rounding
-    float* op = p.out_f32 + ((int64_t)q_row * p.n_heads + head) * D;
+  // partial form and pieces of split units: normalised O in fp32, merged
+  // later without another rounding
+  float* const of32 = slot >= 0 ? p.ws_o + ((int64_t)slot * BQ + (q_row - q_lo)) * D
+                                : (p.out_f32 != nullptr ? p.out_f32 + ((int64_t)q_row * p.n_heads + head) * D : nullptr);
+  float* const lsep = slot >= 0 ? p.ws_lse + (int64_t)slot * BQ + (q_row - q_lo)
+                                : (p.lse != nullptr ? p.lse + (int64_t)head * p.n_q + q_row : nullptr);
+  if (q_ok && of32 != nullptr) {
+    float* op = of32;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -935,18 +960,15 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
       }
   }
-  if (q_ok) {
-    if (p.lse != nullptr && hh == 0) {
-      const float ln2 = 0.69314718055994530942f;
-      p.lse[(int64_t)head * p.n_q + q_row] = any ? (ws.m_run + __log2f(l_tot)) * ln2 : -INFINITY;
-    }
+  if (q_ok && lsep != nullptr && hh == 0) {
+    const float ln2 = 0.69314718055994530942f;
+    *lsep = any ? (ws.m_run + __log2f(l_tot)) * ln2 : -INFINITY;
   }
 }
 
 template <int D, bool SCALED, bool GENERAL>
 hipError_t launch(const AttnParams& p, hipStream_t stream) {
-  const unsigned blocks = (unsigned)(p.n_qt * p.n_heads);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, SCALED, GENERAL>), dim3(blocks), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, SCALED, GENERAL>), dim3((unsigned)p.grid), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 

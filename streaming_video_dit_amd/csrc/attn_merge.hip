@@ -14,12 +14,45 @@
 // written. d/4 lanes own one (query, head) row, 4 columns each: 16-byte fp32
 // loads, 8-byte bf16 stores, consecutive lane groups on consecutive heads of
 // a query, so a wave reads and writes contiguous memory.
+//
+// The same identity merges the two pieces of each split unit of a balanced
+// attn_fwd launch (workspace slots, 256 query rows of one head each).
 #include "sdit_internal.h"
 
 namespace sdit {
 namespace {
 
 constexpr int kThreads = 256;
+
+// Combines n (<= NP) partial results of one (query, head) row at 4 columns:
+// the merged bf16 quad, and the merged LSE in lse_out.
+template <int NP>
+__device__ __forceinline__ uint2 combine4(const float (&lse)[NP], const float4 (&v)[NP], float& lse_out) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) m = fmaxf(m, lse[i]);
+  lse_out = -INFINITY;
+  if (m == -INFINITY) return make_uint2(0u, 0u);   // +0 for a query that sees no key
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    if (lse[i] != -INFINITY) {
+      const float w = expf(lse[i] - m);
+      tot += w;
+      acc.x += w * v[i].x;
+      acc.y += w * v[i].y;
+      acc.z += w * v[i].z;
+      acc.w += w * v[i].w;
+    }
+  }
+  const float inv = 1.0f / tot;
+  const __bf16 b0 = (__bf16)(acc.x * inv), b1 = (__bf16)(acc.y * inv);
+  const __bf16 b2 = (__bf16)(acc.z * inv), b3 = (__bf16)(acc.w * inv);
+  lse_out = m + logf(tot);
+  return make_uint2((uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16),
+                    (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16));
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(MergeParams p) {
@@ -33,38 +66,53 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(MergeParams p) {
   const int64_t oi = pair * D + c;
 
   float lse[kMaxMergeParts];
-  float m = -INFINITY;
+  float4 v[kMaxMergeParts];
 #pragma unroll
   for (int i = 0; i < kMaxMergeParts; ++i) {
     lse[i] = (i < p.n_parts) ? p.lse[i][li] : -INFINITY;
-    m = fmaxf(m, lse[i]);
+    v[i] = lse[i] != -INFINITY ? *reinterpret_cast<const float4*>(p.o[i] + oi) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  uint2 packed = make_uint2(0u, 0u);          // +0 for a query that sees no key
-  float lse_out = -INFINITY;
-  if (m != -INFINITY) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float tot = 0.f;
-#pragma unroll
-    for (int i = 0; i < kMaxMergeParts; ++i) {
-      if (i < p.n_parts && lse[i] != -INFINITY) {
-        const float w = expf(lse[i] - m);
-        const float4 v = *reinterpret_cast<const float4*>(p.o[i] + oi);
-        tot += w;
-        acc.x += w * v.x;
-        acc.y += w * v.y;
-        acc.z += w * v.z;
-        acc.w += w * v.w;
-      }
-    }
-    const float inv = 1.0f / tot;
-    const __bf16 b0 = (__bf16)(acc.x * inv), b1 = (__bf16)(acc.y * inv);
-    const __bf16 b2 = (__bf16)(acc.z * inv), b3 = (__bf16)(acc.w * inv);
-    packed = make_uint2((uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16),
-                        (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16));
-    lse_out = m + logf(tot);
-  }
-  *reinterpret_cast<uint2*>(p.out + oi) = packed;
+  float lse_out;
+  *reinterpret_cast<uint2*>(p.out + oi) = combine4<kMaxMergeParts>(lse, v, lse_out);
   if (p.lse_out != nullptr && c == 0) p.lse_out[li] = lse_out;
+}
+
+// One block per PER_BLOCK rows of one split unit; blocks of slots an XCD
+// does not use (j >= its r) and rows past n_q return at once.
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_split_merge_kernel(AttnParams p, uint16_t* out, float* lse_out) {
+  constexpr int LPR = D / 4;
+  constexpr int PER_BLOCK = kThreads / LPR;
+  constexpr int BLOCKS_PER_UNIT = kAttnBQ / PER_BLOCK;
+  const int unit_slot = blockIdx.x / BLOCKS_PER_UNIT;          // xcd * split_rmax + j
+  const int xcd = unit_slot / p.split_rmax, j = unit_slot % p.split_rmax;
+  const XcdUnits xu = xcd_units(p.n_qt * p.n_heads, xcd, p.cu_per_xcd, true);
+  if (j >= xu.r) return;
+  const int item = xu.u0 + xu.n - xu.r + j;
+  const int head = item / p.n_qt, qt = item % p.n_qt;
+  const int row = (blockIdx.x % BLOCKS_PER_UNIT) * PER_BLOCK + threadIdx.x / LPR;
+  const int q_row = qt * kAttnBQ + row;
+  if (q_row >= p.n_q) return;
+  const int c = (threadIdx.x % LPR) * 4;
+  float lse[2];
+  float4 v[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t r = (int64_t)(2 * unit_slot + i) * kAttnBQ + row;
+    lse[i] = p.ws_lse[r];
+    v[i] = lse[i] != -INFINITY ? *reinterpret_cast<const float4*>(p.ws_o + r * D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float l;
+  *reinterpret_cast<uint2*>(out + ((int64_t)q_row * p.n_heads + head) * D + c) = combine4<2>(lse, v, l);
+  if (lse_out != nullptr && c == 0) lse_out[(int64_t)head * p.n_q + q_row] = l;
+}
+
+template <int D>
+hipError_t launch_split(const AttnParams& p, uint16_t* out, float* lse_out, hipStream_t stream) {
+  constexpr int PER_BLOCK = kThreads / (D / 4);
+  const int64_t blocks = (int64_t)kNumXcd * p.split_rmax * (kAttnBQ / PER_BLOCK);
+  hipLaunchKernelGGL(attn_split_merge_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, out, lse_out);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -81,6 +129,12 @@ hipError_t launch(const MergeParams& p, hipStream_t stream) {
 hipError_t launch_attn_merge(const MergeParams& p, int head_dim, hipStream_t stream) {
   if (p.n_q == 0) return hipSuccess;
   return head_dim == 128 ? launch<128>(p, stream) : launch<64>(p, stream);
+}
+
+hipError_t launch_attn_split_merge(const AttnParams& p, uint16_t* out, float* lse_out, int head_dim,
+                                   hipStream_t stream) {
+  if (p.split_tile == 0 || p.split_rmax == 0) return hipSuccess;
+  return head_dim == 128 ? launch_split<128>(p, out, lse_out, stream) : launch_split<64>(p, out, lse_out, stream);
 }
 
 }  // namespace sdit

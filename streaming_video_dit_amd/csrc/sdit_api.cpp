@@ -4,6 +4,9 @@
 
 #include <math.h>
 #include <stdarg.h>
+
+#include <algorithm>
+#include <atomic>
 #include <stdio.h>
 #include <string.h>
 
@@ -275,6 +278,8 @@ int fill_attn_params(const void* q, int32_t n_q, const sdit_kv_segment* segs, in
     P->n_qb = n_qb;
     P->block_q = block_q;
     P->block_k = block_k;
+    P->grid = n_qt * n_heads;   // one workgroup per unit; a balanced launch re-plans it
+    P->cu_per_xcd = 1;
     const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / sqrt((double)head_dim);
     P->scale_log2 = (float)(scale * 1.4426950408889634073599246810019);
   }
@@ -519,4 +524,166 @@ SDIT_API int sdit_attn_fwd(const void* q, int32_t n_q, const sdit_kv_segment* se
   if (st != SDIT_OK) return st;
   if (n_q == 0) return ok();
   return device_status(sdit::launch_attn_fwd(P, head_dim, (hipStream_t)stream), "attn_fwd");
+}
+
+// ------------------------------------------------------------------ attn_fwd_balanced
+
+namespace {
+
+// Split units per XCD that the workspace bound covers (an XCD has at most 32 CUs).
+constexpr int kMaxCuPerXcd = 32;
+static_assert(SDIT_ATTN_WORKSPACE_BYTES(128) ==
+                  (int64_t)sdit::kNumXcd * (kMaxCuPerXcd - 1) * 2 * sdit::kAttnBQ * (128 + 1) * 4,
+              "workspace bound");
+
+int64_t ws_o_floats(int rmax, int head_dim) { return (int64_t)sdit::kNumXcd * rmax * 2 * sdit::kAttnBQ * head_dim; }
+
+// CUs per XCD of the current device (capped at kMaxCuPerXcd), cached per device.
+int cu_per_xcd(int* c) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "attn_fwd_balanced");
+  if (dev >= 0 && dev < 64 && cache[dev].load(std::memory_order_relaxed) > 0) {
+    *c = cache[dev].load(std::memory_order_relaxed);
+    return SDIT_OK;
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return device_status(e, "attn_fwd_balanced");
+  *c = std::max(1, std::min(kMaxCuPerXcd, cus / sdit::kNumXcd));
+  if (dev >= 0 && dev < 64) cache[dev].store(*c, std::memory_order_relaxed);
+  return SDIT_OK;
+}
+
+// The cut of a balanced launch. On an XCD with r units past its last full
+// wave of C CUs, the r tail pieces queue on the C - r CUs the head pieces
+// leave free, ceil(r / (C - r)) rounds of them; the head piece of t tiles
+// has to outlast those rounds of n - t tiles each, plus a piece's fixed cost
+// (loading its queries, writing its partial) of about kPieceCost tiles. The
+// cut is kept only when it shortens the XCD's run by 5% or more and leaves
+// tail pieces of at least 8 tiles, and not when the partial wave already
+// keeps more than 3/4 of an XCD's CUs busy: measured on MI355X, filling the
+// last few idle CUs does not shorten the run (the busy CUs run faster while
+// the others idle) and the merge then only adds its cost. (Wan chunk, 29 of
+// 32 CUs busy: 2.5% slower with the cut; Large-DiT, 20 of 32: 7% faster.)
+struct BalancedPlan {
+  int tile = 0, rmax = 0, grid = 0;
+};
+
+BalancedPlan plan_balanced(int n_units, int n, int C, int32_t split_tile) {
+  constexpr int kPieceCost = 3;
+  BalancedPlan bp;
+  bp.grid = n_units;
+  if (split_tile == 0 || C < 2 || n < 2) return bp;
+  int rounds = 0, rmax = 0, blocks = 0, waves = 0;
+  for (int x = 0; x < sdit::kNumXcd; ++x) {
+    const sdit::XcdUnits u = sdit::xcd_units(n_units, x, C, true);
+    blocks = std::max(blocks, u.n + u.r);
+    waves = std::max(waves, u.n / C + (u.r > 0 ? 1 : 0));
+    if (u.r == 0) continue;
+    rmax = std::max(rmax, u.r);
+    rounds = std::max(rounds, ceil_div(u.r, C - u.r));
+  }
+  if (rmax == 0) return bp;
+  int t = split_tile;
+  if (t < 0) {
+    if (4 * rmax > 3 * C) return bp;
+    t = (int)(((int64_t)rounds * (n + kPieceCost) + rounds) / (rounds + 1));
+    const int saved = n - t;
+    if (saved < 8 || 20 * (int64_t)saved < (int64_t)waves * n) return bp;
+  }
+  bp.tile = t;
+  bp.rmax = rmax;
+  bp.grid = sdit::kNumXcd * blocks;
+  return bp;
+}
+
+int check_workspace(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs, int32_t n_heads,
+                    int32_t head_dim, const void* out, const float* lse, const void* workspace,
+                    int64_t workspace_bytes, int32_t split_tile) {
+  int64_t tiles = 0;
+  for (int s = 0; s < n_segs; ++s) tiles += ceil_div(segs[s].len, sdit::kAttnBK);
+  if (split_tile < -1 || (split_tile > 0 && split_tile >= tiles))
+    return fail(SDIT_ERR_INVALID, "attn_fwd_balanced: split_tile %d not -1, 0 or in [1, %lld)", split_tile,
+                (long long)tiles);
+  if (n_q == 0) return ok();
+  if (workspace == nullptr || !aligned(workspace, 16))
+    return fail(SDIT_ERR_INVALID, "attn_fwd_balanced: workspace must be non-NULL, 16-byte aligned");
+  if (workspace_bytes < SDIT_ATTN_WORKSPACE_BYTES(head_dim))
+    return fail(SDIT_ERR_INVALID, "attn_fwd_balanced: workspace of %lld bytes < %lld", (long long)workspace_bytes,
+                (long long)SDIT_ATTN_WORKSPACE_BYTES(head_dim));
+  const int64_t rows = (int64_t)n_q * n_heads;
+  if (overlap(workspace, workspace_bytes, q, rows * head_dim * 2) ||
+      overlap(workspace, workspace_bytes, out, rows * head_dim * 2) ||
+      (lse != nullptr && overlap(workspace, workspace_bytes, lse, rows * 4)))
+    return fail(SDIT_ERR_INVALID, "attn_fwd_balanced: workspace overlaps q, out or lse");
+  for (int s = 0; s < n_segs; ++s) {
+    const sdit_kv_segment& sg = segs[s];
+    if (sg.len == 0) continue;
+    const int64_t kv = (int64_t)sg.len * n_heads * head_dim * (sg.dtype == SDIT_INT8 ? 1 : 2);
+    const int64_t sc = (int64_t)sg.len * n_heads * 4;
+    if (overlap(workspace, workspace_bytes, sg.k, kv) || overlap(workspace, workspace_bytes, sg.v, kv) ||
+        (sg.k_scale != nullptr && overlap(workspace, workspace_bytes, sg.k_scale, sc)) ||
+        (sg.v_scale != nullptr && overlap(workspace, workspace_bytes, sg.v_scale, sc)))
+      return fail(SDIT_ERR_INVALID, "attn_fwd_balanced: workspace overlaps segment %d", s);
+  }
+  return ok();
+}
+
+}  // namespace
+
+SDIT_API int sdit_attn_balanced_plan(int32_t n_q, int32_t n_heads, int32_t n_tiles, int32_t n_cus,
+                                      int32_t split_tile, int32_t* tile, int32_t* grid) {
+  if (n_q < 0 || n_heads < 1 || n_tiles < 0 || n_cus < 1 || split_tile < -1 || tile == nullptr || grid == nullptr)
+    return fail(SDIT_ERR_INVALID, "attn_balanced_plan: bad arguments");
+  if ((int64_t)ceil_div(n_q, sdit::kAttnBQ) * n_heads > INT32_MAX / 2)
+    return fail(SDIT_ERR_INVALID, "attn_balanced_plan: grid too large");
+  if (split_tile > 0 && split_tile >= n_tiles)
+    return fail(SDIT_ERR_INVALID, "attn_balanced_plan: split_tile %d >= n_tiles %d", split_tile, n_tiles);
+  const int C = std::max(1, std::min(kMaxCuPerXcd, n_cus / sdit::kNumXcd));
+  const BalancedPlan bp = plan_balanced(ceil_div(n_q, sdit::kAttnBQ) * n_heads, n_tiles, C, split_tile);
+  *tile = bp.tile;
+  *grid = bp.grid;
+  return ok();
+}
+
+SDIT_API int sdit_validate_attn_balanced_args(const void* q, int32_t n_q, const sdit_kv_segment* segs,
+                                              int32_t n_segs, const uint8_t* block_mask, int32_t block_q,
+                                              int32_t block_k, int32_t n_heads, int32_t head_dim,
+                                              float softmax_scale, const void* out, const float* lse,
+                                              const void* workspace, int64_t workspace_bytes, int32_t split_tile) {
+  int st = fill_attn_params(q, n_q, segs, n_segs, block_mask, block_q, block_k, n_heads, head_dim, softmax_scale, out,
+                            lse, nullptr);
+  if (st != SDIT_OK) return st;
+  return check_workspace(q, n_q, segs, n_segs, n_heads, head_dim, out, lse, workspace, workspace_bytes, split_tile);
+}
+
+SDIT_API int sdit_attn_fwd_balanced(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs,
+                                    const uint8_t* block_mask, int32_t block_q, int32_t block_k, int32_t n_heads,
+                                    int32_t head_dim, float softmax_scale, void* out, float* lse, void* workspace,
+                                    int64_t workspace_bytes, int32_t split_tile, void* stream) {
+  sdit::AttnParams P;
+  int st = fill_attn_params(q, n_q, segs, n_segs, block_mask, block_q, block_k, n_heads, head_dim, softmax_scale,
+                            out, lse, &P);
+  if (st != SDIT_OK) return st;
+  st = check_workspace(q, n_q, segs, n_segs, n_heads, head_dim, out, lse, workspace, workspace_bytes, split_tile);
+  if (st != SDIT_OK) return st;
+  if (n_q == 0) return ok();
+  int C = 1;
+  if (split_tile != 0) {
+    st = cu_per_xcd(&C);
+    if (st != SDIT_OK) return st;
+  }
+  const BalancedPlan bp = plan_balanced(P.n_qt * P.n_heads, P.n_tiles, C, split_tile);
+  P.split_tile = bp.tile;
+  P.split_rmax = bp.rmax;
+  P.grid = bp.grid;
+  P.cu_per_xcd = C;
+  P.ws_o = (float*)workspace;
+  P.ws_lse = P.ws_o + ws_o_floats(P.split_rmax, head_dim);
+  st = device_status(sdit::launch_attn_fwd(P, head_dim, (hipStream_t)stream), "attn_fwd_balanced");
+  if (st != SDIT_OK) return st;
+  return device_status(sdit::launch_attn_split_merge(P, (uint16_t*)out, lse, head_dim, (hipStream_t)stream),
+                       "attn_fwd_balanced (merge)");
 }

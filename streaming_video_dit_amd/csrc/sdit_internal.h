@@ -93,10 +93,38 @@ struct AttnParams {
   int32_t block_q;
   int32_t block_k;
   float scale_log2;    // softmax_scale * log2(e)
+  // Balanced launch. The work units (head, query tile) are dealt to the XCDs
+  // in contiguous ranges; on an XCD with R units past its last full wave of
+  // CUs, those R units are cut at candidate tile split_tile into a head piece
+  // [0, split_tile) and a tail piece [split_tile, n_tiles), which write
+  // normalised fp32 O and LSE to workspace slots ((xcd * split_rmax + j) * 2
+  // + piece); attn_split_merge then combines them. split_tile 0: no split.
+  int32_t split_tile;
+  int32_t cu_per_xcd;
+  int32_t split_rmax;  // slots per XCD (largest R)
+  int32_t grid;        // workgroups of the launch
+  float* ws_o;         // [kNumXcd][split_rmax][2][kAttnBQ][head_dim]
+  float* ws_lse;       // [kNumXcd][split_rmax][2][kAttnBQ]
 };
 constexpr int kAttnBQ = 256;  // query rows per workgroup
 constexpr int kAttnBK = 64;   // keys per pipeline stage
+constexpr int kNumXcd = 8;    // XCDs of an MI355X; workgroup b runs on XCD b % 8
 hipError_t launch_attn_fwd(const AttnParams& p, int head_dim, hipStream_t stream);
+
+// Units of a balanced launch on one XCD: the contiguous range [u0, u0 + n)
+// of the n_units work units, of which the last r are split (r = n mod
+// cu_per_xcd when splitting, else 0).
+struct XcdUnits {
+  int32_t u0, n, r;
+};
+__host__ __device__ inline XcdUnits xcd_units(int32_t n_units, int32_t xcd, int32_t cu_per_xcd, bool split) {
+  const int32_t q8 = n_units / kNumXcd, r8 = n_units % kNumXcd;
+  XcdUnits u;
+  u.n = q8 + (xcd < r8 ? 1 : 0);
+  u.u0 = xcd * q8 + (xcd < r8 ? xcd : r8);
+  u.r = split ? u.n % cu_per_xcd : 0;
+  return u;
+}
 
 // ---------------------------------------------------------------- attn_merge
 constexpr int kMaxMergeParts = 8;
@@ -110,6 +138,9 @@ struct MergeParams {
   float* lse_out;                    // fp32 [n_heads][n_q] or NULL
 };
 hipError_t launch_attn_merge(const MergeParams& p, int head_dim, hipStream_t stream);
+// Merge of the two pieces of every split unit of a balanced attn_fwd launch.
+hipError_t launch_attn_split_merge(const AttnParams& p, uint16_t* out, float* lse_out, int head_dim,
+                                   hipStream_t stream);
 
 // ---------------------------------------------------------------- window_permute
 struct PermuteParams {

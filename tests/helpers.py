@@ -68,8 +68,10 @@ def gpu_segments(oracle_segs):
     return out, keep
 
 
-def run_attn(q_bits, oracle_segs, mask, bq, bk, softmax_scale=0.0, lse=True):
-    """HIP attention via the C ABI; returns (out bits [n_q,H,d], lse [H,n_q] or None)."""
+def run_attn(q_bits, oracle_segs, mask, bq, bk, softmax_scale=0.0, lse=True, split_tile=None):
+    """HIP attention via the C ABI; returns (out bits [n_q,H,d], lse [H,n_q] or None).
+    split_tile None: sdit_attn_fwd; else sdit_attn_fwd_balanced with that
+    split_tile (-1 = the library's plan) and a NaN-filled workspace."""
     import torch
     import streaming_video_dit_amd as sdit
     n_q, H, d = q_bits.shape
@@ -78,7 +80,12 @@ def run_attn(q_bits, oracle_segs, mask, bq, bk, softmax_scale=0.0, lse=True):
     m = dev(mask.astype(np.uint8))
     out = torch.full((n_q, H, d), -1, dtype=torch.int16, device="cuda")   # NaN-ish fill (0xFFFF)
     l = torch.full((H, n_q), float("nan"), dtype=torch.float32, device="cuda") if lse else None
-    sdit.attn_fwd(q, n_q, segs, m, bq, bk, H, d, out, l, softmax_scale=softmax_scale)
+    if split_tile is None:
+        sdit.attn_fwd(q, n_q, segs, m, bq, bk, H, d, out, l, softmax_scale=softmax_scale)
+    else:
+        ws = torch.full((sdit.attn_workspace_bytes(d),), 0xFF, dtype=torch.uint8, device="cuda")
+        sdit.attn_fwd_balanced(q, n_q, segs, m, bq, bk, H, d, out, ws, l, softmax_scale=softmax_scale,
+                               split_tile=split_tile)
     torch.cuda.synchronize()
     return host_u16(out), (l.cpu().numpy() if lse else None)
 

@@ -113,6 +113,72 @@ def test_attn_validation():
     assert "segment 1" in (v(segs=_segs(s1=dict(dtype=sdit.SDIT_INT8))), sdit.last_error())[1]
 
 
+def test_attn_balanced_validation():
+    q, out, mask = A16, A16 + 1000 * MB, A16 + 2000 * MB
+    ws = A16 + (1 << 40)
+    need = sdit.attn_workspace_bytes(128)
+    assert need == 8 * 31 * 2 * 256 * 129 * 4          # SDIT_ATTN_WORKSPACE_BYTES(128)
+    header = open(HEADER).read()
+    assert "#define SDIT_ATTN_WORKSPACE_BYTES(head_dim) ((int64_t)8 * 31 * 2 * 256 * ((head_dim) + 1) * 4)" in header
+
+    def v(segs=None, **kw):
+        a = dict(q=q, n_q=300, segs=_segs() if segs is None else segs, block_mask=mask, block_q=128, block_k=128,
+                 n_heads=12, head_dim=128, out=out, lse=None, workspace=ws, workspace_bytes=need, split_tile=-1)
+        a.update(kw)
+        return sdit.validate_attn_balanced_args(**a)
+
+    n_tiles = sum(-(-sg["len"] // 64) for sg in _segs())
+    assert v() == sdit.SDIT_OK
+    assert v(split_tile=0) == sdit.SDIT_OK
+    assert v(split_tile=n_tiles - 1) == sdit.SDIT_OK
+    assert v(split_tile=n_tiles) == sdit.SDIT_ERR_INVALID           # no tail piece left
+    assert v(split_tile=-2) == sdit.SDIT_ERR_INVALID
+    assert v(workspace_bytes=need - 1) == sdit.SDIT_ERR_INVALID
+    assert v(workspace=None) == sdit.SDIT_ERR_INVALID
+    assert v(workspace=ws + 8) == sdit.SDIT_ERR_INVALID               # misaligned
+    assert v(workspace=out - 4096) == sdit.SDIT_ERR_INVALID           # overlaps out
+    assert v(workspace=q) == sdit.SDIT_ERR_INVALID                    # overlaps q
+    assert v(lse=ws + need - 64) == sdit.SDIT_ERR_INVALID             # lse inside the workspace
+    assert v(workspace=_segs()[2]["v"] - 1024) == sdit.SDIT_ERR_INVALID   # overlaps a segment's V
+    assert v(head_dim=80) == sdit.SDIT_ERR_UNSUPPORTED                # the attention checks come first
+    assert v(n_q=0, q=None, out=None, block_mask=None, workspace=None) == sdit.SDIT_OK
+    assert "workspace" in (v(workspace_bytes=16), sdit.last_error())[1]
+
+
+def test_balanced_plan():
+    """The cut rule: on an XCD of C CUs with r units past its last full wave,
+    the r tail pieces take ceil(r / (C - r)) rounds on the free CUs, so the
+    head piece gets t = ceil(rounds (n + 3) / (rounds + 1)) of the n key
+    tiles; no cut when every XCD's units fill whole waves, when some XCD's
+    partial wave keeps more than 3/4 of its CUs busy, or when the cut would
+    save fewer than 8 tiles or under 5% of the XCD's run. Values for a
+    256-CU device (8 XCDs of 32) worked out by hand."""
+    plan = sdit.attn_balanced_plan
+    # Wan chunk: 19 q-tiles x 12 heads = 228 units -> 29 or 28 per XCD, none full:
+    # 29 of 32 CUs busy, more than 3/4, so no cut
+    assert plan(4680, 12, 302, 256) == (0, 228)
+    # forced, it would take 29 + 29 workgroups on the busiest XCD
+    assert plan(4680, 12, 302, 256, split_tile=278) == (278, 8 * (29 + 29))
+    # Large-DiT: 13 x 32 = 416 units -> 52 per XCD = one full wave + 20; 12 free CUs: 2 rounds;
+    # 78 tiles -> t = ceil(2 * 81 / 3) = 54
+    assert plan(3120, 32, 78, 256) == (54, 8 * (52 + 20))
+    # SR: 137 x 12 = 1644 units -> 206 or 205 per XCD = 6 waves + 14 or 13; one round; 545 tiles -> 274
+    assert plan(34848, 12, 545, 256) == (274, 8 * (206 + 14))
+    # exactly whole waves: nothing to cut, one workgroup per unit
+    assert plan(256 * 32, 8, 300, 256) == (0, 256)
+    # 31 of 32 CUs busy: no cut
+    assert plan(256 * 31, 8, 100, 256) == (0, 248)
+    # 24 of 32 busy (exactly 3/4): 3 rounds, 200 tiles -> t = ceil(3 * 203 / 4) = 153
+    assert plan(256 * 24, 8, 200, 256) == (153, 8 * 48)
+    # one unit of 10 tiles: the tail piece would be under 8 tiles
+    assert plan(100, 1, 10, 256) == (0, 1)
+    # a forced cut is taken as given wherever a partial wave exists
+    assert plan(300, 2, 10, 256, split_tile=4) == (4, 8 * 2)
+    assert plan(300, 2, 10, 256, split_tile=0) == (0, 4)
+    with pytest.raises(RuntimeError):
+        plan(300, 2, 10, 256, split_tile=10)
+
+
 def test_attn_partial_validation():
     q, out, mask, lse = A16, A16 + 1000 * MB, A16 + 2000 * MB, A16 + 3000 * MB
 

@@ -386,8 +386,9 @@ def _sample_rows(n_q, rng, k=24):
 @pytest.mark.parametrize("name", ["wan13b", "wan13b_int8", "large_dit", "bsa_sr", "wave_chunks"])
 def test_full_size_hot_path_sampled(name):
     """The benchmark's step at full size: [qknorm_rope3d] -> [kv_quant_int8 of the
-    cache] -> attn_fwd on the GPU; the oracle runs the same chain on the CPU and
-    computes the sampled rows."""
+    cache] -> attention on the GPU, both through attn_fwd and through
+    attn_fwd_balanced with the library's plan (the benchmark's launch); the
+    oracle runs the same chain on the CPU and computes the sampled rows."""
     import torch
     import streaming_video_dit_amd as sdit
     cfg = W.CONFIGS[name]
@@ -407,7 +408,9 @@ def test_full_size_hot_path_sampled(name):
             ck, sk = _gpu_quant(inp.cache_k[i])
             cv, sv = _gpu_quant(inp.cache_v[i])
             gpu_quant[i] = (ck, sk, cv, sv)
-    out, lse = run_attn(gq, segments_for_oracle(inp, gk, gpu_quant), inp.mask, cfg.block, cfg.block)
+    gsegs = segments_for_oracle(inp, gk, gpu_quant)
+    out, lse = run_attn(gq, gsegs, inp.mask, cfg.block, cfg.block)
+    out_b, lse_b = run_attn(gq, gsegs, inp.mask, cfg.block, cfg.block, split_tile=-1)
     # --- oracle chain
     rq, rk = inp.q.copy(), inp.k.copy()
     if cfg.rope:
@@ -429,5 +432,9 @@ def test_full_size_hot_path_sampled(name):
                               rows=rows)
     e = assert_attn_close(out[rows], lse[:, rows], O, LSE, name)
     _say(f"   {len(rows)} rows x {H} heads: max-abs {e[0]:.2e} ({e[2]:.2e} beyond half an ulp), rel-RMS {e[1]:.2e}")
+    e = assert_attn_close(out_b[rows], lse_b[:, rows], O, LSE, name + " balanced")
+    _say(f"   balanced: max-abs {e[0]:.2e} ({e[2]:.2e} beyond half an ulp), rel-RMS {e[1]:.2e}")
     # every row, every head: finite output, and LSE finite where a key is visible
     assert np.all((out & 0x7F80) != 0x7F80)
+    assert np.all((out_b & 0x7F80) != 0x7F80)
+    assert np.array_equal(np.isfinite(lse), np.isfinite(lse_b))
