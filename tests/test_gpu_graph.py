@@ -3,7 +3,9 @@ the stream they are given, so a whole layer-chunk step (qknorm_rope3d,
 kv_quant_int8 of a history cache, attn_fwd over [text bf16 | history int8 |
 current bf16]) can be captured into a HIP graph. Each replay, with unrelated
 eager work and synchronisations between replays, must reproduce the eager
-results bit for bit (the kernels are deterministic)."""
+results bit for bit (the kernels are deterministic). The attention runs
+either as attn_fwd or as attn_fwd_balanced with a cut (attention kernel, then
+the merge of the pieces through the caller's workspace)."""
 import numpy as np
 import pytest
 
@@ -20,7 +22,8 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def test_step_captured_in_a_graph_replays_like_eager():
+@pytest.mark.parametrize("launch", ["plain", "balanced"])
+def test_step_captured_in_a_graph_replays_like_eager(launch):
     import torch
     import streaming_video_dit_amd as sdit
 
@@ -42,12 +45,16 @@ def test_step_captured_in_a_graph_replays_like_eager():
     mask = dev(np.ones((-(-n // 128), nkb), np.uint8))
     segs = sdit.make_segments([dict(k=tk, v=tv, len=64), dict(k=ck, v=cv, k_scale=sk, v_scale=sv, len=L,
                                                                dtype=sdit.SDIT_INT8), dict(k=k, v=v, len=n)])
+    ws = torch.full((sdit.attn_workspace_bytes(d),), 0xFF, dtype=torch.uint8, device="cuda")
 
     def step():
         sdit.qknorm_rope3d(q_in, k_in, q, k, gq, gk, T, Hl, Wl, t0, H, d, dt, dh, dw)
         sdit.kv_quant_int8(hk, ck, sk, L, H, d)
         sdit.kv_quant_int8(hv, cv, sv, L, H, d)
-        sdit.attn_fwd(q, n, segs, mask, 128, 128, H, d, out, lse)
+        if launch == "plain":
+            sdit.attn_fwd(q, n, segs, mask, 128, 128, H, d, out, lse)
+        else:   # 30 key tiles, 6 units: every unit cut at tile 12
+            sdit.attn_fwd_balanced(q, n, segs, mask, 128, 128, H, d, out, ws, lse, split_tile=12)
 
     outputs = (q, k, ck, cv, sk, sv, out, lse)
     step()
