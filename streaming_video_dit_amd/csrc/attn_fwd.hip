@@ -76,12 +76,15 @@
 //    halves), so no per-element compare/select is needed. -1e30 is finite,
 //    so no 0 x inf.
 //  * int8 segments: the per-key K scale (floored at 2^-40, so that the bias
-//    of a masked key stays far below any real score) multiplies score rows and the per-key
-//    V scale multiplies P before its fp16 rounding (no lossy dequantised
-//    copy). Calls with an int8 segment use that scaled path for every tile
-//    (bf16 tiles get scale_log2 and 1); calls without one use the cheaper
-//    unscaled path, with the row sum taken by v_dot2_f32_f16 over the same
-//    fp16 P the MFMA multiplies.
+//    of a masked key stays far below any real score) multiplies score rows
+//    (K itself stays the exact code in bf16). V is staged as code x scale in
+//    fp16: the code is exact in fp16, the row's scale is rounded to fp16 and
+//    the product rounded once (each at most 2^-11 relative, the size of P's
+//    own fp16 rounding); done once per tile while staging, rather than as a
+//    multiply of P in every wave. Calls with an int8 segment use the scaled
+//    path for every tile (bf16 tiles get scale_log2); calls without one
+//    skip the per-key score multiply. Both take the row sum with
+//    v_dot2_f32_f16 over the same fp16 P the MFMA multiplies.
 //  * Grid is remapped so consecutive (head, q-tile) work items land on the
 //    same XCD and share its L2 for K/V.
 //  * Balanced launches (sdit_attn_fwd_balanced): on an XCD whose units leave
@@ -158,7 +161,6 @@ struct Smem {
   uint16_t k[2][BK * Layout<D>::KS];      // bf16, padded rows
   uint16_t v[NVBUF][BK * Layout<D>::VS];  // fp16, padded rows
   float ksc[2][BK];                       // scaled path: per-key multiplier of the raw score
-  float vsc[2][BK];                       // scaled path: per-key multiplier of P
   uint2 desc[LIST_CAP];                   // kept tiles of the current pass (pack_desc)
   int32_t wave_count[NW];
 };
@@ -262,11 +264,18 @@ __device__ __forceinline__ uint4 i8x8_to_f16x8(uint32_t w0, uint32_t w1) {
   const uint2 a = i8x4_to_f16x4(w0), b = i8x4_to_f16x4(w1);
   return make_uint4(a.x, a.y, b.x, b.y);
 }
+// 8 fp16 values times s (packed fp16 multiplies, one rounding each)
+__device__ __forceinline__ uint4 scale_f16x8(uint4 x, f16x2 s) {
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, x.x) * s),
+                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, x.y) * s),
+                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, x.z) * s),
+                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, x.w) * s));
+}
 
 // Registers holding the register-staged part of one tile between its global
 // load and its LDS store. bf16 tiles: VCH chunks of 8 V values. int8 tiles:
-// I8CH chunks of 16 K codes, then I8CH chunks of 16 V codes, and the raw
-// per-key scales.
+// 16 K codes and 16 V codes of one key row, that row's V scale (vs), and
+// (threads 0..BK-1) the K scale of key row tid (ks).
 template <int D, int ST, bool SCALED>
 struct Stage {
   uint4 r[Loader<D, ST>::template sr<SCALED>()];
@@ -335,8 +344,8 @@ __device__ __forceinline__ void issue_kdma(const AttnParams& p, const TileRef& t
 // Register-staged loads of tile t, cut into NPART one-instruction parts so
 // that they can ride on a wave's matrix work (a burst from every wave queues
 // in the CU's address unit). bf16 tiles: V chunks. int8 tiles: K codes, V
-// codes, then the raw per-key scales (commit_tile turns them into
-// multipliers; using them here would wait for the loads).
+// codes, then the scales (commit_tile applies them; using them here would
+// wait for the loads).
 template <int D, int ST, bool SCALED>
 __device__ __forceinline__ void issue_stage_part(const AttnParams& p, const TileRef& t, int head,
                                                  Stage<D, ST, SCALED>& st, const LoadPlan<D, ST>& pl, int j) {
@@ -346,6 +355,7 @@ __device__ __forceinline__ void issue_stage_part(const AttnParams& p, const Tile
   const int row_stride = p.n_heads * D;
   const int64_t base = ((int64_t)t.key0 * p.n_heads + head) * D;
   const bool ragged = t.n_valid < BK;
+  static_assert(!SCALED || LD::I8CH == 1, "a staging thread moves one row's 16 K and 16 V codes");
   if (!SCALED || !t.is_int8) {
     if (j < LD::VCH) {
       const uint16_t* vb = (const uint16_t*)t.v + base;
@@ -366,10 +376,12 @@ __device__ __forceinline__ void issue_stage_part(const AttnParams& p, const Tile
         else
           st.r[LD::I8CH + ji] = *reinterpret_cast<const uint4*>((const int8_t*)t.v + base + off);
       }
-    } else if (j == 2 * LD::I8CH && tid < BK) {
-      const int64_t si = (int64_t)(t.key0 + min(tid, t.n_valid - 1)) * p.n_heads + head;
-      st.ks = t.k_scale[si];
-      st.vs = t.v_scale[si];
+    } else if (j == 2 * LD::I8CH) {
+      if (tid < BK) st.ks = t.k_scale[(int64_t)(t.key0 + min(tid, t.n_valid - 1)) * p.n_heads + head];
+      if (LD::I8_THREADS >= ST || tid < LD::I8_THREADS) {
+        const int row = min(tid / (D / 16), t.n_valid - 1);   // this thread's V row
+        st.vs = t.v_scale[(int64_t)(t.key0 + row) * p.n_heads + head];
+      }
     }
   }
 }
@@ -407,16 +419,19 @@ __device__ __forceinline__ void commit_tile(const AttnParams& p, const TileRef& 
       const uint4 kc = st.r[j], vc = st.r[LD::I8CH + j];
       *reinterpret_cast<uint4*>(kr) = i8x8_to_bf16x8(kc.x, kc.y);
       *reinterpret_cast<uint4*>(kr + 8) = i8x8_to_bf16x8(kc.z, kc.w);
-      *reinterpret_cast<uint4*>(vr) = i8x8_to_f16x8(vc.x, vc.y);
-      *reinterpret_cast<uint4*>(vr + 8) = i8x8_to_f16x8(vc.z, vc.w);
+      // V = code * scale in fp16: the exact fp16 code times the row's scale
+      // rounded to fp16, one rounding of the product
+      const _Float16 sv = (_Float16)st.vs;
+      const f16x2 sv2 = {sv, sv};
+      *reinterpret_cast<uint4*>(vr) = scale_f16x8(i8x8_to_f16x8(vc.x, vc.y), sv2);
+      *reinterpret_cast<uint4*>(vr + 8) = scale_f16x8(i8x8_to_f16x8(vc.z, vc.w), sv2);
     }
   }
   if (SCALED && tid < BK) {
-    // per-key multipliers of the raw score (log2 units) and of P; keys past the
-    // segment end keep a positive K multiplier so that their bias stays -1e30
+    // per-key multipliers of the raw score (log2 units); keys past the segment
+    // end keep a positive multiplier so that their bias stays -1e30
     const bool ok = tid < t.n_valid;
     sm.ksc[kbuf][tid] = (t.is_int8 && ok) ? fmaxf(st.ks * p.scale_log2, KSC_MIN) : p.scale_log2;
-    sm.vsc[kbuf][tid] = ok ? (t.is_int8 ? st.vs : 1.0f) : 0.0f;
   }
 }
 
@@ -463,7 +478,7 @@ struct WaveState {
 // score subtile kt is key kt*32 + 8*(e2/4) + 4*hh + e2%4 of the tile.
 template <int D, bool SCALED, bool GENERAL, typename Hook, typename Tail>
 __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t, WaveState<D>& ws,
-                                           const uint16_t* kl, const float* ksc, const float* vsc, int k_lane,
+                                           const uint16_t* kl, const float* ksc, int k_lane,
                                            int r, int hh, int my_qb, int qb_lo, int n_qbt, f16x8 (&pb)[4],
                                            Hook&& after_mfma, Tail&& after_scores) {
   using L = Layout<D>;
@@ -574,32 +589,18 @@ __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t
     float pv[16];
 #pragma unroll
     for (int e2 = 0; e2 < 16; ++e2) pv[e2] = __builtin_amdgcn_exp2f(fmaf(s[kt][e2], cs, -m_use));
-    if (SCALED) {
-#pragma unroll
-      for (int e2 = 0; e2 < 16; ++e2) ws.l_run += pv[e2];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 sc = *reinterpret_cast<const float4*>(&vsc[kt * 32 + 8 * g + 4 * hh]);
-        pv[4 * g + 0] *= sc.x;
-        pv[4 * g + 1] *= sc.y;
-        pv[4 * g + 2] *= sc.z;
-        pv[4 * g + 3] *= sc.w;
-      }
-    }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       f16x8 v;
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = (_Float16)pv[8 * half + j];
       pb[2 * kt + half] = v;
-      if (!SCALED) {
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          f16x2 pr;
-          pr[0] = v[j];
-          pr[1] = v[j + 1];
-          ws.l_run = __builtin_amdgcn_fdot2(pr, ones, ws.l_run, false);
-        }
+      for (int j = 0; j < 8; j += 2) {
+        f16x2 pr;
+        pr[0] = v[j];
+        pr[1] = v[j + 1];
+        ws.l_run = __builtin_amdgcn_fdot2(pr, ones, ws.l_run, false);
       }
     }
   }
@@ -631,13 +632,13 @@ __device__ __forceinline__ void pv_tile(WaveState<D>& ws, const uint16_t* vl, in
 template <int D, bool SCALED, bool GENERAL, int ST, int PF, typename Ride>
 __device__ __forceinline__ void lead_tile_scaled(const AttnParams& p, const TileRef& t, const TileRef& tn, int head,
                                                  WaveState<D>& ws, const uint16_t* __restrict__ kcur,
-                                                 const float* __restrict__ ksc, const float* __restrict__ vsc,
+                                                 const float* __restrict__ ksc,
                                                  const uint16_t* __restrict__ vcur, uint16_t* __restrict__ knew,
                                                  bool dma, const LoadPlan<D, ST>& plan, int k_lane, int v_lane,
                                                  int r, int hh, int my_qb, int qb_lo, int n_qbt, f16x8 (&pb)[4],
                                                  Ride&& ride) {
   if (dma) issue_kdma_to<D, ST>(p, tn, head, knew, plan);
-  qk_softmax<D, SCALED, GENERAL>(p, t, ws, kcur, ksc, vsc, k_lane, r, hh, my_qb, qb_lo, n_qbt, pb, ride, [] {});
+  qk_softmax<D, SCALED, GENERAL>(p, t, ws, kcur, ksc, k_lane, r, hh, my_qb, qb_lo, n_qbt, pb, ride, [] {});
   pv_tile<D, PF>(ws, vcur, v_lane, pb);
 }
 
@@ -822,7 +823,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         pending = false;
         if ((t.wmask >> wave) & 1) {
           qk_softmax<D, SCALED, GENERAL>(
-              p, t, ws, sm.k[kbuf], sm.ksc[kbuf], sm.vsc[kbuf], k_lane, r, hh, my_qb, qb_lo, n_qbt, pb,
+              p, t, ws, sm.k[kbuf], sm.ksc[kbuf], k_lane, r, hh, my_qb, qb_lo, n_qbt, pb,
               [&](int i) {
                 if (stager && has_next && i % STRIDE == 0 && i / STRIDE < NPART)
                   issue_stage_part<D, ST, SCALED>(p, tn, head, st, plan, i / STRIDE);
@@ -893,7 +894,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
           if (has1) commit_tile<D, ST, SCALED>(p, tn1, st, sm, knext, vnext);
           if (compute) {
             lead_tile_scaled<D, SCALED, GENERAL, ST, PF_PV>(p, t, tn1, head, ws, sm.k[kbuf], sm.ksc[kbuf],
-                                                            sm.vsc[kbuf], sm.v[vbuf], sm.k[knext], dma, plan,
+                                                            sm.v[vbuf], sm.k[knext], dma, plan,
                                                             k_lane, v_lane, r, hh, my_qb, qb_lo, n_qbt, pb, ride);
           } else {
             if (dma) issue_kdma<D, ST>(p, tn1, head, sm, knext, plan);
@@ -904,7 +905,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
           pending = false;
           if (has1) commit_tile<D, ST, SCALED>(p, tn1, st, sm, knext, vnext);
           if (compute) {
-            qk_softmax<D, SCALED, GENERAL>(p, t, ws, sm.k[kbuf], sm.ksc[kbuf], sm.vsc[kbuf], k_lane, r, hh, my_qb,
+            qk_softmax<D, SCALED, GENERAL>(p, t, ws, sm.k[kbuf], sm.ksc[kbuf], k_lane, r, hh, my_qb,
                                            qb_lo, n_qbt, pb, ride, none);
             pending = true;
           } else if (has2) {
