@@ -599,11 +599,15 @@ BalancedPlan plan_balanced(int n_units, int n, int C, int32_t split_tile) {
   return bp;
 }
 
-int check_workspace(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs, int32_t n_heads,
+int check_workspace(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs,
+                    const uint8_t* block_mask, int32_t block_q, int32_t block_k, int32_t n_heads,
                     int32_t head_dim, const void* out, const float* lse, const void* workspace,
                     int64_t workspace_bytes, int32_t split_tile) {
-  int64_t tiles = 0;
-  for (int s = 0; s < n_segs; ++s) tiles += ceil_div(segs[s].len, sdit::kAttnBK);
+  int64_t tiles = 0, kbs = 0;
+  for (int s = 0; s < n_segs; ++s) {
+    tiles += ceil_div(segs[s].len, sdit::kAttnBK);
+    kbs += ceil_div(segs[s].len, block_k);
+  }
   if (split_tile < -1 || (split_tile > 0 && split_tile >= tiles))
     return fail(SDIT_ERR_INVALID, "attn_fwd_balanced: split_tile %d not -1, 0 or in [1, %lld)", split_tile,
                 (long long)tiles);
@@ -616,8 +620,9 @@ int check_workspace(const void* q, int32_t n_q, const sdit_kv_segment* segs, int
   const int64_t rows = (int64_t)n_q * n_heads;
   if (overlap(workspace, workspace_bytes, q, rows * head_dim * 2) ||
       overlap(workspace, workspace_bytes, out, rows * head_dim * 2) ||
-      (lse != nullptr && overlap(workspace, workspace_bytes, lse, rows * 4)))
-    return fail(SDIT_ERR_INVALID, "attn_fwd_balanced: workspace overlaps q, out or lse");
+      (lse != nullptr && overlap(workspace, workspace_bytes, lse, rows * 4)) ||
+      overlap(workspace, workspace_bytes, block_mask, (int64_t)ceil_div(n_q, block_q) * kbs))
+    return fail(SDIT_ERR_INVALID, "attn_fwd_balanced: workspace overlaps q, out, lse or block_mask");
   for (int s = 0; s < n_segs; ++s) {
     const sdit_kv_segment& sg = segs[s];
     if (sg.len == 0) continue;
@@ -656,7 +661,8 @@ SDIT_API int sdit_validate_attn_balanced_args(const void* q, int32_t n_q, const 
   int st = fill_attn_params(q, n_q, segs, n_segs, block_mask, block_q, block_k, n_heads, head_dim, softmax_scale, out,
                             lse, nullptr);
   if (st != SDIT_OK) return st;
-  return check_workspace(q, n_q, segs, n_segs, n_heads, head_dim, out, lse, workspace, workspace_bytes, split_tile);
+  return check_workspace(q, n_q, segs, n_segs, block_mask, block_q, block_k, n_heads, head_dim, out, lse, workspace,
+                         workspace_bytes, split_tile);
 }
 
 SDIT_API int sdit_attn_fwd_balanced(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs,
@@ -667,7 +673,8 @@ SDIT_API int sdit_attn_fwd_balanced(const void* q, int32_t n_q, const sdit_kv_se
   int st = fill_attn_params(q, n_q, segs, n_segs, block_mask, block_q, block_k, n_heads, head_dim, softmax_scale,
                             out, lse, &P);
   if (st != SDIT_OK) return st;
-  st = check_workspace(q, n_q, segs, n_segs, n_heads, head_dim, out, lse, workspace, workspace_bytes, split_tile);
+  st = check_workspace(q, n_q, segs, n_segs, block_mask, block_q, block_k, n_heads, head_dim, out, lse, workspace,
+                       workspace_bytes, split_tile);
   if (st != SDIT_OK) return st;
   if (n_q == 0) return ok();
   int C = 1;

@@ -140,6 +140,8 @@ def test_attn_balanced_validation():
     assert v(workspace=q) == sdit.SDIT_ERR_INVALID                    # overlaps q
     assert v(lse=ws + need - 64) == sdit.SDIT_ERR_INVALID             # lse inside the workspace
     assert v(workspace=_segs()[2]["v"] - 1024) == sdit.SDIT_ERR_INVALID   # overlaps a segment's V
+    assert v(workspace=mask - need + 16) == sdit.SDIT_ERR_INVALID     # ends inside the block mask
+    assert v(workspace=mask - need) == sdit.SDIT_OK                   # ends where the mask starts
     assert v(head_dim=80) == sdit.SDIT_ERR_UNSUPPORTED                # the attention checks come first
     assert v(n_q=0, q=None, out=None, block_mask=None, workspace=None) == sdit.SDIT_OK
     assert "workspace" in (v(workspace_bytes=16), sdit.last_error())[1]
