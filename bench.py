@@ -260,9 +260,9 @@ def cpu_baseline(cfg: W.Config, budget_s: float = 10.0):
         dt, dh, dw = cfg.split
         for c in range(cfg.n_chunks):
             r = W.chunk_rows(cfg, c)
-            t0 = cfg.t0 + c * cfg.T
-            rq[r] = oracle.qknorm_rope3d(inp.q[r], inp.gamma_q, cfg.T, cfg.Hl, cfg.Wl, t0, dt, dh, dw)
-            rk[r] = oracle.qknorm_rope3d(inp.k[r], inp.gamma_k, cfg.T, cfg.Hl, cfg.Wl, t0, dt, dh, dw)
+            f0 = cfg.t0 + c * cfg.T   # the chunk's first frame position
+            rq[r] = oracle.qknorm_rope3d(inp.q[r], inp.gamma_q, cfg.T, cfg.Hl, cfg.Wl, f0, dt, dh, dw)
+            rk[r] = oracle.qknorm_rope3d(inp.k[r], inp.gamma_k, cfg.T, cfg.Hl, cfg.Wl, f0, dt, dh, dw)
     segs = []
     for i, (k, v) in enumerate(zip(inp.cache_k, inp.cache_v)):
         if cfg.seg_int8[i]:
@@ -287,6 +287,7 @@ def cpu_baseline(cfg: W.Config, budget_s: float = 10.0):
     el = time.perf_counter() - t0
     flops = W.attn_flops(cfg, inp.mask) * heads / cfg.n_heads
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": el,
             "sample": f"{cfg.name}: qknorm_rope3d of the whole chunk"
                       f"{' + int8 quantisation of the cache' if any(cfg.seg_int8) else ''}"
                       f" + attention for {heads} of {cfg.n_heads} heads, fp64 numpy, {el:.1f} s"}
