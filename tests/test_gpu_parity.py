@@ -275,6 +275,30 @@ def test_attention_long_cache_several_passes(case):
     _say(f"   max-abs {e[0]:.2e} ({e[2]:.2e} beyond half an ulp), rel-RMS {e[1]:.2e}")
 
 
+def test_attention_maximum_head_count():
+    """The largest head count the library accepts (65536, so that a 64-key
+    tile's rows, n_heads * head_dim elements apart, stay within 32-bit
+    offsets: 2^29 elements at d = 128), with a full and a ragged key tile:
+    65536 workgroups, K and V of 1.1 GB each. The oracle computes sampled
+    heads (first, last and some between); every head's output is finite."""
+    H, d, L = 65536, 128, 65
+    _say("attention at the maximum head count: generating inputs")
+    q = W.normal_bf16(83, 0, (1, H, d))
+    k = W.normal_bf16(83, 1, (L, H, d))
+    v = W.normal_bf16(83, 2, (L, H, d))
+    segs = [{"k": k, "v": v, "dtype": "bf16"}]
+    mask = np.ones((1, 1), np.uint8)
+    _say("   running", H, "heads")
+    out, lse = run_attn(q, segs, mask, 128, 128)
+    assert np.all((out & 0x7F80) != 0x7F80) and np.all(np.isfinite(lse))
+    heads = [0, 1, 4097, 32768, 65534, 65535]
+    # heads are independent: the oracle runs on the sampled heads' slices
+    sub = [{"k": np.ascontiguousarray(k[:, heads]), "v": np.ascontiguousarray(v[:, heads]), "dtype": "bf16"}]
+    O, LSE = oracle.attention(np.ascontiguousarray(q[:, heads]), sub, mask, 128, 128)
+    e = assert_attn_close(out[:, heads], lse[heads], O, LSE, "maximum head count")
+    _say(f"   {len(heads)} heads: max-abs {e[0]:.2e} ({e[2]:.2e} beyond half an ulp), rel-RMS {e[1]:.2e}")
+
+
 def test_dense_block_mask_matches_sdpa_within_the_pages_figure():
     """FlashVSR deployment notes (Block-Sparse-Attention on Ada): with a dense
     mask the block-sparse kernel has to reproduce scaled_dot_product_attention,
