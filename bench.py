@@ -298,7 +298,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="wan13b", choices=sorted(W.CONFIGS))
+    ap.add_argument("--workload", default="wan13b", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--kv-parts", type=int, default=1,
@@ -335,7 +335,7 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "launches": max(1, args.steps)}), flush=True)
         return
 
-    cfg = W.CONFIGS[args.workload]
+    cfg = W.WORKLOADS[args.workload]
     step = Step(cfg, torch, sdit, args.kv_parts, args.launch, args.split_tile)
     for _ in range(args.warmup):
         step.run()

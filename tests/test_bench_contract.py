@@ -18,7 +18,7 @@ sys.path.insert(0, ROOT)
 
 def test_cpu_baseline_times_the_oracle_it_ran():
     import bench
-    cfg = W.CONFIGS["tiny"]            # RoPE on, first frame position 2
+    cfg = W.WORKLOADS["tiny"]            # RoPE on, first frame position 2
     t = time.perf_counter()
     r = bench.cpu_baseline(cfg, budget_s=0.2)
     wall = time.perf_counter() - t

@@ -15,7 +15,7 @@ from oracle import attention
 
 @pytest.mark.parametrize("name", ["tiny_chunks"])
 def test_chunk_causal_mask_equals_per_chunk_attention(name):
-    cfg = W.CONFIGS[name]
+    cfg = W.WORKLOADS[name]
     inp = W.make_inputs(cfg)
     segs = [{"k": k, "v": v, "dtype": "bf16"} for k, v in zip(inp.cache_k, inp.cache_v)]
     segs += [{"k": inp.k[W.chunk_rows(cfg, c)], "v": inp.v[W.chunk_rows(cfg, c)], "dtype": "bf16"}
@@ -33,7 +33,7 @@ def test_chunk_causal_mask_equals_per_chunk_attention(name):
 
 
 def test_chunk_layout_and_mask_shape():
-    cfg = W.CONFIGS["wave_chunks"]
+    cfg = W.WORKLOADS["wave_chunks"]
     assert cfg.chunk_tokens == 4680 and cfg.chunk_slot == 4736 and cfg.n_q == 4 * 4736
     assert cfg.n_cached == 2 and cfg.seg_lens[2:] == [4680] * 4
     m = W.make_mask(cfg)

@@ -147,7 +147,7 @@ def test_norm_zero_tokens_is_a_no_op(op):
 @pytest.mark.parametrize("op", OPS)
 @pytest.mark.parametrize("name", ["wan13b", "large_dit", "bsa_sr"])
 def test_norm_workload_shapes_sampled(op, name):
-    cfg = W.CONFIGS[name]
+    cfg = W.WORKLOADS[name]
     n, d = cfg.n_q, cfg.n_heads * cfg.head_dim
     inp = W.make_norm_inputs(cfg.seed, n, d, offset=1.0)
     _say(op, name, n, d)

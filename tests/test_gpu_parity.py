@@ -43,7 +43,7 @@ def _gpu_quant(x_bits):
 
 
 def test_kv_quant_bit_exact_on_the_int8_cache_workload():
-    cfg = W.CONFIGS["wan13b_int8"]
+    cfg = W.WORKLOADS["wan13b_int8"]
     inp = W.make_inputs(cfg)
     for name, x in [("text K", inp.cache_k[0]), ("text V", inp.cache_v[0]),
                     ("history K", inp.cache_k[1]), ("history V", inp.cache_v[1]), ("chunk K", inp.k)]:
@@ -102,7 +102,7 @@ def _check_rope(got, x_bits, g, geo):
 
 @pytest.mark.parametrize("name", ["tiny", "wan13b", "large_dit"])
 def test_qknorm_rope3d_within_one_ulp(name):
-    cfg = W.CONFIGS[name]
+    cfg = W.WORKLOADS[name]
     inp = W.make_inputs(cfg)
     geo = (cfg.T, cfg.Hl, cfg.Wl, cfg.t0, cfg.split)
     _say("qknorm_rope3d", name, inp.q.shape)
@@ -112,7 +112,7 @@ def test_qknorm_rope3d_within_one_ulp(name):
 
 
 def test_qknorm_rope3d_in_place_equals_out_of_place():
-    cfg = W.CONFIGS["wan13b"]
+    cfg = W.WORKLOADS["wan13b"]
     inp = W.make_inputs(cfg, n_heads=3)
     geo = (cfg.T, cfg.Hl, cfg.Wl, cfg.t0, cfg.split)
     a = _gpu_rope(geo, inp.q, inp.k, inp.gamma_q, inp.gamma_k)
@@ -153,7 +153,7 @@ def test_qknorm_rope3d_other_splits(split, d):
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_dense"])
 def test_tiny_workload_end_to_end(name):
-    cfg = W.CONFIGS[name]
+    cfg = W.WORKLOADS[name]
     inp = W.make_inputs(cfg)
     geo = (cfg.T, cfg.Hl, cfg.Wl, cfg.t0, cfg.split)
     _say("tiny end to end", name)
@@ -171,7 +171,7 @@ def test_tiny_workload_end_to_end(name):
 
 def test_tiny_chunks_end_to_end():
     """Two query chunks in one forward, RoPE per chunk, chunk-causal mask."""
-    cfg = W.CONFIGS["tiny_chunks"]
+    cfg = W.WORKLOADS["tiny_chunks"]
     inp = W.make_inputs(cfg)
     dt, dh, dw = cfg.split
     gq, gk, rq, rk = inp.q.copy(), inp.k.copy(), inp.q.copy(), inp.k.copy()
@@ -190,11 +190,11 @@ def test_tiny_chunks_end_to_end():
 
 
 def test_tiny_mask_readings_differ_on_gpu():
-    cfg = W.CONFIGS["tiny"]
+    cfg = W.WORKLOADS["tiny"]
     inp = W.make_inputs(cfg)
     segs = segments_for_oracle(inp, inp.k)
     a, _ = run_attn(inp.q, segs, W.make_mask(cfg), 16, 16)
-    b, _ = run_attn(inp.q, segs, W.make_mask(W.CONFIGS["tiny_dense"]), 16, 16)
+    b, _ = run_attn(inp.q, segs, W.make_mask(W.WORKLOADS["tiny_dense"]), 16, 16)
     assert np.array_equal(a[16:], b[16:])
     assert not np.array_equal(a[:16], b[:16])
 
@@ -415,7 +415,7 @@ def test_full_size_hot_path_sampled(name):
     oracle runs the same chain on the CPU and computes the sampled rows."""
     import torch
     import streaming_video_dit_amd as sdit
-    cfg = W.CONFIGS[name]
+    cfg = W.WORKLOADS[name]
     inp = W.make_inputs(cfg)
     H, d, n_q = cfg.n_heads, cfg.head_dim, cfg.n_q
     _say("full size", name, "n_q", n_q, "keys", sum(cfg.seg_lens))

@@ -179,7 +179,7 @@ def test_wan_chunk_split_cache_and_current_sampled():
     history) and the current chunk: GPU partials and merge against the
     oracle's whole-cache attention on sampled rows, and against the
     single-launch GPU path on every row."""
-    cfg = W.CONFIGS["wan13b"]
+    cfg = W.WORKLOADS["wan13b"]
     inp = W.make_inputs(cfg)
     H, d, n_q, B = cfg.n_heads, cfg.head_dim, cfg.n_q, cfg.block
     segs = [{"k": k, "v": v, "dtype": "bf16"} for k, v in zip(inp.cache_k, inp.cache_v)]

@@ -76,7 +76,7 @@ def _chain(cfg, inp, rows=None):
 
 
 def test_tiny_windowed_attention_every_element():
-    cfg = W.CONFIGS["tiny_local"]
+    cfg = W.WORKLOADS["tiny_local"]
     inp = W.make_inputs(cfg)
     _say("tiny windowed attention")
     out, lse, O, LSE = _chain(cfg, inp)
@@ -85,7 +85,7 @@ def test_tiny_windowed_attention_every_element():
 
 
 def test_clip_windowed_attention_sampled():
-    cfg = W.CONFIGS["vsr_local"]
+    cfg = W.WORKLOADS["vsr_local"]
     inp = W.make_inputs(cfg)
     n = cfg.n_q
     rng = np.random.default_rng(cfg.seed)

@@ -83,7 +83,7 @@ def test_dense_equals_torch_sdpa_fp64():
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_dense"])
 def test_tiny_workload_against_brute_force(name):
-    cfg = W.CONFIGS[name]
+    cfg = W.WORKLOADS[name]
     inp = W.make_inputs(cfg)
     dt, dh, dw = cfg.split
     qr = qknorm_rope3d(inp.q, inp.gamma_q, cfg.T, cfg.Hl, cfg.Wl, cfg.t0, dt, dh, dw)
@@ -96,7 +96,7 @@ def test_tiny_workload_against_brute_force(name):
 
 
 def test_tiny_mask_readings_differ():
-    cfg_c, cfg_d = W.CONFIGS["tiny"], W.CONFIGS["tiny_dense"]
+    cfg_c, cfg_d = W.WORKLOADS["tiny"], W.WORKLOADS["tiny_dense"]
     inp = W.make_inputs(cfg_c)
     segs = _segs(inp.cache_k + [inp.k], inp.cache_v + [inp.v])
     Oc, _ = attention(inp.q, segs, W.make_mask(cfg_c), 16, 16)

@@ -9,7 +9,7 @@ from oracle import local_window_mask
 
 @pytest.mark.parametrize("name", ["vsr_local", "tiny_local"])
 def test_workload_local_mask_equals_oracle(name):
-    cfg = W.CONFIGS[name]
+    cfg = W.WORKLOADS[name]
     m = W.make_mask(cfg)
     ref = local_window_mask(cfg.T, cfg.Hl, cfg.Wl, cfg.window, cfg.local_range)
     assert np.array_equal(m, ref)

@@ -21,7 +21,7 @@ def test_px_per_token_is_vae_times_patch():
 
 def test_wan_chunk_geometry():
     for name in ("wan13b", "wan13b_int8", "wave_chunks"):
-        cfg = W.CONFIGS[name]
+        cfg = W.WORKLOADS[name]
         assert cfg.Hl == G["wan_height_px"] // G["px_per_token"]
         assert cfg.Wl == G["wan_width_px"] // G["px_per_token"]
         assert cfg.T % G["latent_frames_per_chunk_divisor"] == 0
@@ -32,14 +32,14 @@ def test_wan_chunk_geometry():
 
 
 def test_sr_clip_geometry():
-    cfg = W.CONFIGS["bsa_sr"]
+    cfg = W.WORKLOADS["bsa_sr"]
     side = G["sr_clip_px"] // G["px_per_token"]
     assert (cfg.Hl, cfg.Wl) == (side, side)
     assert cfg.seg_lens == [cfg.T * side * side] and cfg.n_q == cfg.seg_lens[0]
 
 
 def test_windowed_clip_geometry():
-    cfg = W.CONFIGS["vsr_local"]
+    cfg = W.WORKLOADS["vsr_local"]
     w_px, h_px = G["vsr_timing_clip_px"]
     assert (cfg.Hl, cfg.Wl) == (h_px // G["px_per_token"], w_px // G["px_per_token"])
     assert cfg.window == G["block_tokens_side"] and cfg.block == cfg.window ** 2

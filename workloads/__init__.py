@@ -129,7 +129,7 @@ class Config:
         return sum(-(-L // self.block) for L in self.seg_lens)
 
 
-CONFIGS: Dict[str, Config] = {
+WORKLOADS: Dict[str, Config] = {
     # Tiny: 1 head x d64, 2 latent frames of 4x4 tokens, cache 16 text + 32
     # history (two frames) + 32 current, block 16.
     "tiny": Config("tiny", 1, 64, 2, 4, 4, 2, [16, 32, 32], [False, False, False], 16,
@@ -175,8 +175,8 @@ CONFIGS: Dict[str, Config] = {
                           description="tiny, two chunks in one forward"),
 }
 
-# Order used by the configs list of the workload definition.
-CONFIG_ORDER = ["tiny", "wan13b", "wan13b_int8", "large_dit", "bsa_sr"]
+# The five main workloads, smallest (the one the oracle runs in full) first.
+WORKLOAD_ORDER = ["tiny", "wan13b", "wan13b_int8", "large_dit", "bsa_sr"]
 
 
 def make_mask(cfg: Config) -> np.ndarray:
