@@ -217,6 +217,77 @@ def measure_norms(cfg: W.Config, torch, sdit, steps: int, warmup: int):
     return res
 
 
+def _time_rotating(torch, fn, n_sets: int, steps: int, warmup: int):
+    """Median, p10 and p90 (us) of single launches fn(i), timed with HIP
+    events on the current stream, cycling through n_sets buffer sets."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i % n_sets)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(i % n_sets)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    return float(np.median(us)), float(np.percentile(us, 10)), float(np.percentile(us, 90))
+
+
+def _hbm_entry(kernel: str, shape, nbytes: int, n_sets: int, t):
+    med, p10, p90 = t
+    gbs = nbytes / (med * 1e-6) / 1e9
+    return {"kernel": kernel, "shape": list(shape), "bound": "hbm", "us_median": round(med, 2),
+            "us_p10_p90": [round(p10, 2), round(p90, 2)], "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes, "input_sets": n_sets}
+
+
+def measure_hbm_kernels(cfg: W.Config, torch, sdit, steps: int, warmup: int):
+    """The HBM-bound kernels of the step, each launch timed alone: qknorm_rope3d
+    of the chunk's q and k (2 * 2 * 2 bytes per element: q and k read and
+    written, plus the two fp32 gamma vectors), and kv_quant_int8 (2 bytes read,
+    1 written per element, 4 per (token, head) scale) of the chunk's K and of
+    the cached segments' K. Successive launches cycle through enough buffer
+    sets to exceed 768 MB, so the 256 MB last-level cache does not serve them."""
+    H, d, n = cfg.n_heads, cfg.head_dim, cfg.n_q
+    res = {}
+
+    def sets_for(nbytes):
+        return max(3, -(-768 * 2**20 // nbytes))
+
+    if cfg.rope:
+        inp = W.make_inputs(cfg)
+        r = W.chunk_rows(cfg, 0)
+        q0, k0 = inp.q[r], inp.k[r]
+        m = q0.shape[0]
+        dt, dh, dw = cfg.split
+        nbytes = 2 * 2 * 2 * m * H * d + 2 * 4 * d
+        ns = sets_for(nbytes)
+        qs = [_dev(q0, torch) for _ in range(ns)]
+        ks = [_dev(k0, torch) for _ in range(ns)]
+        qo = [torch.empty_like(qs[0]) for _ in range(ns)]
+        ko = [torch.empty_like(ks[0]) for _ in range(ns)]
+        gq, gk = _dev(inp.gamma_q, torch), _dev(inp.gamma_k, torch)
+        t = _time_rotating(torch, lambda i: sdit.qknorm_rope3d(qs[i], ks[i], qo[i], ko[i], gq, gk, cfg.T, cfg.Hl, cfg.Wl,
+                                                               cfg.t0, H, d, dt, dh, dw, cfg.theta, cfg.eps),
+                           ns, steps, warmup)
+        res["qknorm_rope3d_chunk"] = _hbm_entry(f"qknorm_rope3d_kernel<{d}>", (m, H, d), nbytes, ns, t)
+        del qs, ks, qo, ko
+    n_cache = sum(cfg.seg_lens[:cfg.n_cached])
+    for label, n_tok in (("kv_quant_int8_chunk", cfg.chunk_tokens), ("kv_quant_int8_cache", n_cache)):
+        if n_tok == 0:
+            continue
+        nbytes = n_tok * H * d * 3 + n_tok * H * 4
+        ns = sets_for(nbytes)
+        x = W.normal_bf16(cfg.seed, 90, (n_tok, H, d))
+        xs = [_dev(x, torch) for _ in range(ns)]
+        cs = [torch.empty((n_tok, H, d), dtype=torch.int8, device="cuda") for _ in range(ns)]
+        ss = [torch.empty((n_tok, H), dtype=torch.float32, device="cuda") for _ in range(ns)]
+        t = _time_rotating(torch, lambda i: sdit.kv_quant_int8(xs[i], cs[i], ss[i], n_tok, H, d), ns, steps, warmup)
+        res[label] = _hbm_entry(f"kv_quant_int8_kernel<{d}>", (n_tok, H, d), nbytes, ns, t)
+        del xs, cs, ss
+    return res
+
+
 def attn_src_hash() -> str:
     """sha256 prefix of the attention kernels' sources (attn_fwd.hip, then
     attn_merge.hip, which holds the merge of a balanced launch)."""
@@ -307,6 +378,8 @@ def main():
                     help="attention entry point: sdit_attn_fwd_balanced (library plan) or sdit_attn_fwd")
     ap.add_argument("--split-tile", type=int, default=-1,
                     help="balanced launch: key tile of the cut (-1: the library's plan, 0: none)")
+    ap.add_argument("--with-hbm", action="store_true",
+                    help="also time qknorm_rope3d and kv_quant_int8 alone (rotated input sets) against 8 TB/s")
     ap.add_argument("--with-norms", action="store_true",
                     help="also time RMSNorm and LayerNorm + modulate on the workload's hidden-state shape")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -406,6 +479,8 @@ def main():
                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": step.merge_bytes}
         rec["roofline"]["traffic"] = None
+    if args.with_hbm:
+        rec["hbm_kernels"] = measure_hbm_kernels(cfg, torch, sdit, args.steps, args.warmup)
     if args.with_norms:
         rec["norms"] = measure_norms(cfg, torch, sdit, args.steps, args.warmup)
     if not args.no_cpu_baseline:
