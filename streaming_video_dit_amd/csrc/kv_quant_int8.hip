@@ -6,8 +6,16 @@
 //   amax = max |x|, scale = amax / 127 (IEEE binary32 division),
 //   code = clamp(rint(x / scale), -127, 127)  (binary32 quotient, ties to even),
 //   amax == 0 -> scale 0, codes 0.
-// Rounding is fully specified so the codes are unique; hipcc's default
-// correctly rounded fp32 division and v_rndne_f32 implement it exactly.
+// Rounding is fully specified so the codes are unique. The quotient x / scale
+// is the correctly rounded binary32 one, computed without a division per
+// element (Markstein's correction): y = RN(1/scale), an fp64 quotient rounded
+// to binary32 (1/scale for a binary32 scale is never within 2^-49 relative of
+// a binary32 rounding boundary, so this double rounding is exact);
+// q0 = RN(x * y) is within one ulp of x / scale; the residual x - q0 * scale
+// is exact in one fma; and RN(q0 + residual * y) = RN(x / scale) (Markstein's
+// theorem, for y within half an ulp of 1/scale and no underflow). Rows with
+// scale < 2^-100 keep the plain division, so every intermediate stays normal.
+// v_rndne_f32 then rounds to the nearest code, ties to even.
 //
 // HBM-bound: each row is read once (2*d bytes) and written once (d + 4 bytes).
 // A row is handled by d/8 lanes (16 B loaded per lane); each lane keeps
@@ -59,11 +67,19 @@ __global__ __launch_bounds__(kThreads) void kv_quant_int8_kernel(QuantParams p) 
 
     const float scale = amax / 127.0f;
     uint32_t packed[2] = {0u, 0u};
-    if (amax > 0.f) {
+    if (scale >= 0x1p-100f) {
+      const float y = (float)(1.0 / (double)scale);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float c = rintf(x[i] / scale);
-        c = fminf(fmaxf(c, -127.f), 127.f);
+        const float q0 = x[i] * y;
+        const float q = fmaf(fmaf(-q0, scale, x[i]), y, q0);
+        const float c = fminf(fmaxf(rintf(q), -127.f), 127.f);
+        packed[i / 4] |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * (i % 4));
+      }
+    } else if (amax > 0.f) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float c = fminf(fmaxf(rintf(x[i] / scale), -127.f), 127.f);
         packed[i / 4] |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * (i % 4));
       }
     }
