@@ -14,6 +14,8 @@ from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsdit.so")
+# test-only build of the same library with a one-tile-at-a-time attention schedule
+SINGLE_STAGE_LIB_PATH = os.path.join(HERE, "libsdit_single_stage.so")
 
 SDIT_OK, SDIT_ERR_INVALID, SDIT_ERR_UNSUPPORTED, SDIT_ERR_DEVICE = 0, 1, 2, 3
 SDIT_BF16, SDIT_INT8 = 0, 1
@@ -36,11 +38,17 @@ _i32, _f32, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 def lib() -> ctypes.CDLL:
     """The loaded libsdit.so (loaded on first use; raises if it was not built)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m streaming_video_dit_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = load_library(LIB_PATH)
+    return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a build of the sdit library (libsdit.so, or the test-only
+    libsdit_single_stage.so) and declare the C signatures."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m streaming_video_dit_amd.build`")
+    L = ctypes.CDLL(path)
     L.sdit_abi_version.restype = ctypes.c_int
     L.sdit_status_string.restype = ctypes.c_char_p
     L.sdit_status_string.argtypes = [ctypes.c_int]
@@ -78,8 +86,7 @@ def lib() -> ctypes.CDLL:
               "sdit_attn_balanced_plan"):
         getattr(L, n).restype = ctypes.c_int
     if L.sdit_abi_version() != ABI_VERSION:
-        raise ImportError(f"libsdit.so ABI {L.sdit_abi_version()} != binding ABI {ABI_VERSION}")
-    _lib = L
+        raise ImportError(f"{path} ABI {L.sdit_abi_version()} != binding ABI {ABI_VERSION}")
     return L
 
 
@@ -175,13 +182,15 @@ def make_segments(segs: Sequence[dict]):
 
 
 def attn_fwd(q, n_q: int, segs, block_mask, block_q: int, block_k: int, n_heads: int, head_dim: int,
-             out, lse=None, softmax_scale: float = 0.0, stream=None) -> None:
+             out, lse=None, softmax_scale: float = 0.0, stream=None, library=None) -> None:
     """sdit_attn_fwd. ``segs`` is a list of dicts (see make_segments) or a
-    ctypes array made by make_segments."""
+    ctypes array made by make_segments. ``library``: another build loaded
+    with load_library (default libsdit.so)."""
     arr = segs if isinstance(segs, ctypes.Array) else make_segments(segs)
     n = len(segs)
-    _check(lib().sdit_attn_fwd(_ptr(q), n_q, arr, n, _ptr(block_mask), block_q, block_k, n_heads, head_dim,
-                              softmax_scale, _ptr(out), _ptr(lse), _stream(stream)))
+    L = library if library is not None else lib()
+    _check(L.sdit_attn_fwd(_ptr(q), n_q, arr, n, _ptr(block_mask), block_q, block_k, n_heads, head_dim,
+                           softmax_scale, _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def attn_workspace_bytes(head_dim: int) -> int:
@@ -191,16 +200,17 @@ def attn_workspace_bytes(head_dim: int) -> int:
 
 def attn_fwd_balanced(q, n_q: int, segs, block_mask, block_q: int, block_k: int, n_heads: int, head_dim: int,
                       out, workspace, lse=None, softmax_scale: float = 0.0, split_tile: int = -1,
-                      workspace_bytes=None, stream=None) -> None:
+                      workspace_bytes=None, stream=None, library=None) -> None:
     """sdit_attn_fwd_balanced: ``workspace`` is device memory of at least
     attn_workspace_bytes(head_dim) bytes (its size is taken from the tensor
     unless ``workspace_bytes`` is given)."""
     arr = segs if isinstance(segs, ctypes.Array) else make_segments(segs)
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().sdit_attn_fwd_balanced(_ptr(q), n_q, arr, len(segs), _ptr(block_mask), block_q, block_k, n_heads,
-                                       head_dim, softmax_scale, _ptr(out), _ptr(lse), _ptr(workspace),
-                                       workspace_bytes, split_tile, _stream(stream)))
+    L = library if library is not None else lib()
+    _check(L.sdit_attn_fwd_balanced(_ptr(q), n_q, arr, len(segs), _ptr(block_mask), block_q, block_k, n_heads,
+                                    head_dim, softmax_scale, _ptr(out), _ptr(lse), _ptr(workspace),
+                                    workspace_bytes, split_tile, _stream(stream)))
 
 
 def attn_balanced_plan(n_q: int, n_heads: int, n_tiles: int, n_cus: int, split_tile: int = -1):

@@ -2,7 +2,12 @@
 
     python -m streaming_video_dit_amd.build
 
-writes streaming_video_dit_amd/libsdit.so next to this file.
+writes streaming_video_dit_amd/libsdit.so next to this file, and beside it
+libsdit_single_stage.so: the same library with the attention kernel's
+pipelined schedule replaced by a one-tile-at-a-time schedule
+(SDIT_SINGLE_STAGE=1), which exists only so that tests can check that the
+prefetching schedule gives bit-identical results. The two compile in
+parallel.
 """
 from __future__ import annotations
 
@@ -15,6 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsdit.so")
+LIB_SINGLE_STAGE = os.path.join(HERE, "libsdit_single_stage.so")
 
 SOURCES = ["sdit_api.cpp", "qknorm_rope3d.hip", "kv_quant_int8.hip", "attn_fwd.hip", "attn_merge.hip", "window_permute.hip",
            "norms.hip"]
@@ -36,21 +42,36 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
+def _command(out: str, extra_flags) -> list:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + FLAGS + list(extra_flags or []) + ["-I", os.path.join(ROOT, "include"), "-o", tmp] + srcs
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    return [hipcc()] + FLAGS + list(extra_flags or []) + ["-I", os.path.join(ROOT, "include"), "-o", out] + srcs
+
+
+def _finish(proc, cmd, tmp, lib, verbose):
+    out, err = proc.communicate()
     # the host pass does not know the packed-fp32 feature and says so; anything else is shown
     noise = "'-packed-fp32-ops' is not a recognized feature"
-    msgs = [l for l in (r.stdout + r.stderr).splitlines() if noise not in l and l.strip()]
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    msgs = [l for l in (out + err).splitlines() if noise not in l and l.strip()]
+    if proc.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Build libsdit.so and libsdit_single_stage.so (in parallel); returns the
+    path of libsdit.so."""
+    jobs = []
+    for lib, flags in ((LIB, list(extra_flags or [])),
+                       (LIB_SINGLE_STAGE, list(extra_flags or []) + ["-DSDIT_SINGLE_STAGE=1"])):
+        tmp = lib + ".tmp"
+        cmd = _command(tmp, flags)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True), cmd, tmp, lib))
+    for proc, cmd, tmp, lib in jobs:
+        _finish(proc, cmd, tmp, lib, verbose)
     return LIB
 
 

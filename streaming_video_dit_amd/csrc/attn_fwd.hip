@@ -96,6 +96,8 @@
 //    the keys together.
 #include "sdit_internal.h"
 
+#include <type_traits>
+
 namespace sdit {
 namespace {
 
@@ -121,6 +123,15 @@ constexpr float MASK_BIAS = -1.0e30f; // added to scores of keys that must not c
 constexpr float MASKED_MAX = -1.0e15f;
 constexpr float KSC_MIN = 0x1p-40f;   // floor of the per-key score multiplier
 constexpr int NXCD = kNumXcd;
+// A test-only build (SDIT_SINGLE_STAGE=1) replaces the pipelined schedules by
+// one that loads a tile, waits, and computes it with every wave, one tile at
+// a time. Each wave then does the same arithmetic on the same tiles in the
+// same order, so its results must match the pipelined kernel bit for bit
+// (a drifting prefetch would show up as a difference).
+#ifndef SDIT_SINGLE_STAGE
+#define SDIT_SINGLE_STAGE 0
+#endif
+constexpr bool kSingleStage = SDIT_SINGLE_STAGE != 0;
 static_assert(BQ == NW * 32, "one wave per 32 query rows");
 
 template <int D>
@@ -163,6 +174,7 @@ struct Smem {
   float ksc[2][BK];                       // scaled path: per-key multiplier of the raw score
   uint2 desc[LIST_CAP];                   // kept tiles of the current pass (pack_desc)
   int32_t wave_count[NW];
+  float vmax[NW];   // every wave's largest staged V magnitude (exact form)
 };
 
 struct TileInfo {
@@ -237,6 +249,67 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 w) {
   return make_uint4(pack_f16(bf16_lo(w.x), bf16_hi(w.x)), pack_f16(bf16_lo(w.y), bf16_hi(w.y)),
                     pack_f16(bf16_lo(w.z), bf16_hi(w.z)), pack_f16(bf16_lo(w.w), bf16_hi(w.w)));
+}
+// the same, each value times 2^e before its one rounding to fp16
+__device__ __forceinline__ uint32_t pack_f16_exp(float a, float b, int e) { return pack_f16(ldexpf(a, e), ldexpf(b, e)); }
+__device__ __forceinline__ uint4 bf16x8_to_f16x8_exp(uint4 w, int e) {
+  return make_uint4(pack_f16_exp(bf16_lo(w.x), bf16_hi(w.x), e), pack_f16_exp(bf16_lo(w.y), bf16_hi(w.y), e),
+                    pack_f16_exp(bf16_lo(w.z), bf16_hi(w.z), e), pack_f16_exp(bf16_lo(w.w), bf16_hi(w.w), e));
+}
+// largest magnitude among 8 bf16 values and m
+__device__ __forceinline__ float absmax_bf16x8(uint4 w, float m) {
+  m = fmaxf(m, fmaxf(fabsf(bf16_lo(w.x)), fabsf(bf16_hi(w.x))));
+  m = fmaxf(m, fmaxf(fabsf(bf16_lo(w.y)), fabsf(bf16_hi(w.y))));
+  m = fmaxf(m, fmaxf(fabsf(bf16_lo(w.z)), fabsf(bf16_hi(w.z))));
+  return fmaxf(m, fmaxf(fabsf(bf16_lo(w.w)), fabsf(bf16_hi(w.w))));
+}
+
+// ---- V exponents. P.V multiplies fp16 P with fp16 V. bf16 V converts to fp16
+// exactly only between 2^-17 and 65280 in magnitude (below, fp16 has too few
+// bits; above, it overflows), and an int8 row's V = code * fp16(scale) keeps
+// 11 bits only while the scale is a normal fp16 (>= 2^-14). So every 64-key V
+// tile is staged as V * 2^e, one exponent for the whole tile chosen from its
+// largest magnitude M (bf16 tiles: max |v|; int8 tiles: the largest V scale):
+// e = 0 while M lies in the band below, else the multiple of 16 that brings M
+// into it. A wave folds 2^(e - e_prev) into its fp32 O accumulators whenever
+// the exponent of the tiles it multiplies changes (an exact power-of-two
+// rescale, like the lazy max) and 2^-e into the final 1/l. Within a tile every
+// staged value then carries at most 2^-11 relative error, or 2^-17 M absolute
+// for elements more than 2^14 below the tile's largest (the fp16 subnormal
+// step), and nothing overflows: P <= 2^8 times |V 2^e| < 2^16 per product.
+constexpr float V_BF16_LO = 0x1p-8f, V_BF16_HI = 0x1p16f;   // bf16 band [2^-8, 2^16)
+constexpr float V_I8_LO = 0x1p-8f, V_I8_HI = 0x1p8f;        // int8 scale band [2^-8, 2^8)
+
+__device__ __forceinline__ int band_exponent(float m, float lo, float hi) {
+  if (!(m > 0.f) || (m >= lo && m < hi) || !(m < INFINITY)) return 0;
+  const int k = __builtin_amdgcn_frexp_expf(m) - 1;   // m in [2^k, 2^(k+1))
+  // floor((k + 8) / 16) for negative k + 8 too
+  const int f = (k + 8) >= 0 ? (k + 8) / 16 : -((15 - (k + 8)) / 16);
+  return -16 * f;
+}
+__device__ __forceinline__ int v_exponent(float m, bool is_int8) {
+  return is_int8 ? band_exponent(m, V_I8_LO, V_I8_HI) : band_exponent(m, V_BF16_LO, V_BF16_HI);
+}
+
+// largest value of x over the wave (x >= 0), returned in every lane
+__device__ __forceinline__ float wave_max(float x) {
+  auto dpp = [](float v, int ctrl) -> float {
+    switch (ctrl) {
+      case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+      case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+      case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
+      default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));
+    }
+  };
+  x = fmaxf(x, dpp(x, 0));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp(x, 1));   // quad_perm [2,3,0,1]: every quad holds its max
+  x = fmaxf(x, dpp(x, 2));   // row_half_mirror: groups of 8
+  x = fmaxf(x, dpp(x, 3));   // row_mirror: rows of 16
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
 // 8 int8 codes (two words) -> 8 bf16 / 8 fp16 (exact: |code| <= 128)
@@ -394,21 +467,48 @@ __device__ __forceinline__ void issue_stage(const AttnParams& p, const TileRef& 
     issue_stage_part<D, ST, SCALED>(p, t, head, st, pl, j);
 }
 
+// Largest magnitude of this thread's staged share of a tile: max |v| of a
+// bf16 tile's V chunks, or the V scale of an int8 tile's row (0 for threads
+// that stage nothing of it).
+template <int D, int ST, bool SCALED>
+__device__ __forceinline__ float staged_magnitude(const TileRef& t, const Stage<D, ST, SCALED>& st) {
+  using LD = Loader<D, ST>;
+  float m = 0.f;
+  if (!SCALED || !t.is_int8) {
+#pragma unroll
+    for (int j = 0; j < LD::VCH; ++j) m = absmax_bf16x8(st.r[j], m);
+  } else if (LD::I8_THREADS >= ST || (int)threadIdx.x < LD::I8_THREADS) {
+    m = st.vs;
+  }
+  return m;
+}
+
+// The bf16 V chunks of a staged tile into LDS buffer vdst, times 2^e.
+template <int D, int ST, bool SCALED>
+__device__ __forceinline__ void store_v_bf16(const Stage<D, ST, SCALED>& st, uint16_t* vdst, int e) {
+  using L = Layout<D>;
+  using LD = Loader<D, ST>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < LD::VCH; ++j) {
+    const int lin = tid + j * ST;
+    const int row = lin / L::CPR, c = lin % L::CPR;
+    *reinterpret_cast<uint4*>(vdst + row * L::VS + c * 8) =
+        e == 0 ? bf16x8_to_f16x8(st.r[j]) : bf16x8_to_f16x8_exp(st.r[j], e);
+  }
+}
+
 // Finish tile t: register-staged V (and int8 K) into LDS buffers vbuf (kbuf),
-// scaled-path multipliers into slot kbuf.
+// scaled-path multipliers into slot kbuf; V times 2^e (see v_exponent).
+// min_scale keeps the smallest positive int8 V row scale committed.
 template <int D, int ST, bool SCALED>
 __device__ __forceinline__ void commit_tile(const AttnParams& p, const TileRef& t, const Stage<D, ST, SCALED>& st,
-                                            Smem<D>& sm, int kbuf, int vbuf) {
+                                            Smem<D>& sm, int kbuf, int vbuf, int e, float& min_scale) {
   using L = Layout<D>;
   using LD = Loader<D, ST>;
   const int tid = threadIdx.x;
   if (!SCALED || !t.is_int8) {
-#pragma unroll
-    for (int j = 0; j < LD::VCH; ++j) {
-      const int lin = tid + j * ST;
-      const int row = lin / L::CPR, c = lin % L::CPR;
-      *reinterpret_cast<uint4*>(sm.v[vbuf] + row * L::VS + c * 8) = bf16x8_to_f16x8(st.r[j]);
-    }
+    store_v_bf16<D, ST, SCALED>(st, sm.v[vbuf], e);
   } else if (LD::I8_THREADS >= ST || tid < LD::I8_THREADS) {
 #pragma unroll
     for (int j = 0; j < LD::I8CH; ++j) {
@@ -419,9 +519,10 @@ __device__ __forceinline__ void commit_tile(const AttnParams& p, const TileRef& 
       const uint4 kc = st.r[j], vc = st.r[LD::I8CH + j];
       *reinterpret_cast<uint4*>(kr) = i8x8_to_bf16x8(kc.x, kc.y);
       *reinterpret_cast<uint4*>(kr + 8) = i8x8_to_bf16x8(kc.z, kc.w);
-      // V = code * scale in fp16: the exact fp16 code times the row's scale
-      // rounded to fp16, one rounding of the product
-      const _Float16 sv = (_Float16)st.vs;
+      // V 2^e = code * scale 2^e in fp16: the exact fp16 code times the row's
+      // scale 2^e (exact in fp32) rounded to fp16, one rounding of the product
+      const _Float16 sv = (_Float16)ldexpf(st.vs, e);
+      min_scale = fminf(min_scale, st.vs > 0.f ? st.vs : INFINITY);
       const f16x2 sv2 = {sv, sv};
       *reinterpret_cast<uint4*>(vr) = scale_f16x8(i8x8_to_f16x8(vc.x, vc.y), sv2);
       *reinterpret_cast<uint4*>(vr + 8) = scale_f16x8(i8x8_to_f16x8(vc.z, vc.w), sv2);
@@ -469,6 +570,7 @@ struct WaveState {
   float m_run;         // running max, log2 units
   float l_run;         // this lane's half of the row sum
   bool seen;           // general masks: a kept key reached this row
+  int e_o;             // o holds O * 2^e_o (the V exponent of the tiles last multiplied)
 };
 
 // First half of a 64-key tile for one wave: S^T = K Q^T, masking bias,
@@ -476,11 +578,11 @@ struct WaveState {
 // runs after the i-th of the 2*D/16 score MFMAs, after_scores() after the
 // last one. Element e2 of
 // score subtile kt is key kt*32 + 8*(e2/4) + 4*hh + e2%4 of the tile.
-template <int D, bool SCALED, bool GENERAL, typename Hook, typename Tail>
+template <int D, bool SCALED, bool GENERAL, bool EXACT, typename Hook, typename Tail>
 __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t, WaveState<D>& ws,
                                            const uint16_t* kl, const float* ksc, int k_lane,
                                            int r, int hh, int my_qb, int qb_lo, int n_qbt, f16x8 (&pb)[4],
-                                           Hook&& after_mfma, Tail&& after_scores) {
+                                           int e, Hook&& after_mfma, Tail&& after_scores) {
   using L = Layout<D>;
   constexpr int NKS = D / 16;
   constexpr int NDT = D / 32;
@@ -567,17 +669,28 @@ __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t
   mt = swap_halves_max(mt) * cs;
   if (mt < MASKED_MAX) mt = -INFINITY;   // nothing visible for this row in the tile
 
-  // ---- online softmax (lazy running max)
+  // ---- online softmax (lazy running max). The same rare branch brings o to
+  // the tile's V exponent e (exact power-of-two rescale), before the P.V of
+  // this tile adds to it.
   const bool need = mt > ws.m_run + TAU;
-  if (__ballot(need)) {
+  if (__ballot(need) || (EXACT && e != ws.e_o)) {
     const float m_new = need ? mt : ws.m_run;
     const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(ws.m_run - m_new);
     ws.m_run = m_new;
     ws.l_run *= alpha;
+    const int sh = EXACT ? e - ws.e_o : 0;
+    ws.e_o = EXACT ? e : ws.e_o;
+    if (sh == 0) {
 #pragma unroll
-    for (int i = 0; i < NDT; ++i)
+      for (int i = 0; i < NDT; ++i)
 #pragma unroll
-      for (int e2 = 0; e2 < 16; ++e2) ws.o[i][e2] *= alpha;
+        for (int e2 = 0; e2 < 16; ++e2) ws.o[i][e2] *= alpha;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int e2 = 0; e2 < 16; ++e2) ws.o[i][e2] = ldexpf(ws.o[i][e2] * alpha, sh);
+    }
   }
   const float m_use = (ws.m_run == -INFINITY) ? 0.f : ws.m_run;
 
@@ -607,7 +720,8 @@ __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t
 }
 
 // Second half of a tile: O^T += V^T P^T (transposed reads of the row-major
-// fp16 V tile).
+// fp16 V tile, which holds V * 2^e; qk_softmax of the tile has brought o to
+// the same exponent).
 template <int D, int PF>
 __device__ __forceinline__ void pv_tile(WaveState<D>& ws, const uint16_t* vl, int v_lane, const f16x8 (&pb)[4]) {
   constexpr int NPV = 4 * (D / 32);
@@ -629,16 +743,16 @@ __device__ __forceinline__ void pv_tile(WaveState<D>& ws, const uint16_t* vl, in
 // buffer being filled and does not make them wait for those loads (with one
 // shared buffer object it waited for the whole load before the first score
 // MFMA).
-template <int D, bool SCALED, bool GENERAL, int ST, int PF, typename Ride>
+template <int D, bool SCALED, bool GENERAL, bool EXACT, int ST, int PF, typename Ride>
 __device__ __forceinline__ void lead_tile_scaled(const AttnParams& p, const TileRef& t, const TileRef& tn, int head,
                                                  WaveState<D>& ws, const uint16_t* __restrict__ kcur,
                                                  const float* __restrict__ ksc,
                                                  const uint16_t* __restrict__ vcur, uint16_t* __restrict__ knew,
                                                  bool dma, const LoadPlan<D, ST>& plan, int k_lane, int v_lane,
                                                  int r, int hh, int my_qb, int qb_lo, int n_qbt, f16x8 (&pb)[4],
-                                                 Ride&& ride) {
+                                                 Ride&& ride, int e) {
   if (dma) issue_kdma_to<D, ST>(p, tn, head, knew, plan);
-  qk_softmax<D, SCALED, GENERAL>(p, t, ws, kcur, ksc, k_lane, r, hh, my_qb, qb_lo, n_qbt, pb, ride, [] {});
+  qk_softmax<D, SCALED, GENERAL, EXACT>(p, t, ws, kcur, ksc, k_lane, r, hh, my_qb, qb_lo, n_qbt, pb, e, ride, [] {});
   pv_tile<D, PF>(ws, vcur, v_lane, pb);
 }
 
@@ -650,6 +764,20 @@ __device__ __forceinline__ uint32_t wave_qbits(const AttnParams& p, int q_lo, in
   const int r1 = min(p.n_q, r0 + 32) - 1;
   const int b0 = r0 / p.block_q - qb_lo, b1 = r1 / p.block_q - qb_lo;
   return ((2u << b1) - 1u) & ~((1u << b0) - 1u);
+}
+
+// Exact V exponent of a staged tile (every wave calls it; one barrier): the
+// largest magnitude over all staging threads' shares.
+template <int D>
+__device__ __forceinline__ int exact_v_exponent(Smem<D>& sm, float m, bool is_int8, int wave, int lane) {
+  const float wm = wave_max(m);
+  if (lane == 0) sm.vmax[wave] = wm;
+  __syncthreads();
+  float mm = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) mm = fmaxf(mm, sm.vmax[w]);
+  mm = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mm)));
+  return v_exponent(mm, is_int8);
 }
 
 template <int D, bool SCALED, bool GENERAL>
@@ -723,6 +851,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   ws.m_run = -INFINITY;
   ws.l_run = 0.f;
   ws.seen = !GENERAL;
+  ws.e_o = 0;
 
   // per-lane LDS offsets (elements) that do not change over the loop
   const int k_lane = r * L::KS + 8 * hh;
@@ -744,6 +873,20 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
   for (int w = 0; w < NW; ++w) wq[w] = wave_qbits(p, q_lo, qb_lo, w);
 
+  // Every pass over the kept tiles, in one of two forms. The fast form
+  // stages every V tile as it is (exponent 0); it is exact while each int8
+  // row scale is 0 or a normal fp16 (>= 2^-14) and every staged value is
+  // finite, and otherwise off by at most 2^-25 per bf16 element (values below
+  // 2^-17, where fp16 has fewer bits). The exact form settles every tile's V
+  // exponent from its largest magnitude before the tile is committed (one
+  // more barrier per tile). The workgroup runs the fast form, checks its
+  // result (below), and runs the exact form from the start only when the
+  // check fails.
+  // fast form: smallest positive int8 row scale this thread staged (a float,
+  // not a flag: a per-lane flag would live in scalar registers the loop needs)
+  float i8_min_scale = INFINITY;
+  auto all_passes = [&](auto exact_tag) {
+    constexpr bool EXACT = decltype(exact_tag)::value;
 #pragma unroll 1
   for (int cbase = c_lo; cbase < c_hi; cbase += LIST_CAP) {
     // ---- compact the kept tiles of this pass into sm.list (order preserved),
@@ -791,7 +934,30 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     __syncthreads();
     if (total == 0) continue;
 
-    if constexpr (!SCALED) {
+    if constexpr (kSingleStage) {
+      // ---- single-stage schedule (test-only build): V buffer 0, K buffers
+      // alternating (one fixed K buffer trips the compiler's address-space
+      // handling of the direct-to-LDS loads)
+#pragma unroll 1
+      for (int it = 0; it < total; ++it) {
+        const TileRef t = tile_ref(p, sm.desc[it]);
+        const bool direct_k = SCALED ? (k_wave && !t.is_int8) : stager;
+        if (direct_k) issue_kdma<D, ST>(p, t, head, sm, it & 1, plan);
+        if (stager) issue_stage<D, ST, SCALED>(p, t, head, st, plan);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        int e = 0;
+        if (EXACT) e = exact_v_exponent(sm, stager ? staged_magnitude<D, ST, SCALED>(t, st) : 0.f, t.is_int8, wave, lane);
+        if (stager) commit_tile<D, ST, SCALED>(p, t, st, sm, it & 1, 0, e, i8_min_scale);
+        __syncthreads();
+        if ((t.wmask >> wave) & 1) {
+          f16x8 pb[4];
+          qk_softmax<D, SCALED, GENERAL, EXACT>(p, t, ws, sm.k[it & 1], sm.ksc[it & 1], k_lane, r, hh, my_qb, qb_lo,
+                                                n_qbt, pb, e, [](int) {}, [] {});
+          pv_tile<D, PF_PV>(ws, sm.v[0], v_lane, pb);
+        }
+        __syncthreads();
+      }
+    } else if constexpr (!SCALED) {
       // ---- unscaled kernels: the four leading waves move every tile one
       // step ahead. Tile i lives in K buffer i%2 and V buffer i%3. During
       // step i the leading waves' V loads of tile i+1 ride on their score
@@ -805,7 +971,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       if (stager) {
         issue_kdma<D, ST>(p, tn, head, sm, 0, plan);
         issue_stage<D, ST, SCALED>(p, tn, head, st, plan);
-        commit_tile<D, ST, SCALED>(p, tn, st, sm, 0, 0);
+        commit_tile<D, ST, SCALED>(p, tn, st, sm, 0, 0, 0, i8_min_scale);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
@@ -819,11 +985,22 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         const int knext = kbuf ^ 1;
         const int vnext = (vbuf + 1 == NVBUF) ? 0 : vbuf + 1;
         if (has_next) tn = tile_ref(p, sm.desc[it + 1]);
+        // exact form: tile it's V exponent from its largest magnitude; the
+        // stagers, whose registers still hold its bf16 V, store it again
+        // times 2^e when e is not 0
+        int e_it = 0;
+        if constexpr (EXACT) {
+          e_it = exact_v_exponent(sm, stager ? staged_magnitude<D, ST, SCALED>(t, st) : 0.f, false, wave, lane);
+          if (e_it != 0) {
+            if (stager) store_v_bf16<D, ST, SCALED>(st, sm.v[vbuf], e_it);
+            __syncthreads();
+          }
+        }
         if (lagging && pending) pv_tile<D, PF_PV>(ws, sm.v[vprev], v_lane, pb);
         pending = false;
         if ((t.wmask >> wave) & 1) {
-          qk_softmax<D, SCALED, GENERAL>(
-              p, t, ws, sm.k[kbuf], sm.ksc[kbuf], k_lane, r, hh, my_qb, qb_lo, n_qbt, pb,
+          qk_softmax<D, SCALED, GENERAL, EXACT>(
+              p, t, ws, sm.k[kbuf], sm.ksc[kbuf], k_lane, r, hh, my_qb, qb_lo, n_qbt, pb, e_it,
               [&](int i) {
                 if (stager && has_next && i % STRIDE == 0 && i / STRIDE < NPART)
                   issue_stage_part<D, ST, SCALED>(p, tn, head, st, plan, i / STRIDE);
@@ -839,7 +1016,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
           issue_kdma<D, ST>(p, tn, head, sm, knext, plan);
           issue_stage<D, ST, SCALED>(p, tn, head, st, plan);
         }
-        if (has_next && stager) commit_tile<D, ST, SCALED>(p, tn, st, sm, knext, vnext);
+        if (has_next && stager) commit_tile<D, ST, SCALED>(p, tn, st, sm, knext, vnext, 0, i8_min_scale);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         vprev = vbuf;
@@ -854,7 +1031,9 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       TileRef tc = tile_ref(p, sm.desc[0]);
       if (k_wave && !tc.is_int8) issue_kdma<D, ST>(p, tc, head, sm, 0, plan);
       issue_stage<D, ST, SCALED>(p, tc, head, st, plan);
-      commit_tile<D, ST, SCALED>(p, tc, st, sm, 0, 0);
+      int e_cur = 0;
+      if constexpr (EXACT) e_cur = exact_v_exponent(sm, staged_magnitude<D, ST, SCALED>(tc, st), tc.is_int8, wave, lane);
+      commit_tile<D, ST, SCALED>(p, tc, st, sm, 0, 0, e_cur, i8_min_scale);
       TileRef tn1 = tc;
       if (total > 1) {
         tn1 = tile_ref(p, sm.desc[1]);
@@ -871,7 +1050,9 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       // matrix); waves 4..7 first multiply the previous tile's P with V, then
       // commit, then run scores + softmax of tile i, keeping P for the next
       // step (matrix, vector, matrix, vector), so on every SIMD the two waves
-      // alternate between the matrix and the vector units.
+      // alternate between the matrix and the vector units. In the exact form
+      // the V exponent of tile i+1 is settled at the top of step i (one
+      // barrier), before anyone commits it.
       f16x8 pb[4];
       bool pending = false;   // lagging waves: P of the previous tile awaits its P.V
       int kbuf = 0, vbuf = 0, vprev = NVBUF - 1;
@@ -883,6 +1064,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         const int vnext = (vbuf + 1 == NVBUF) ? 0 : vbuf + 1;
         TileRef tn2 = tn1;
         if (has2) tn2 = tile_ref(p, sm.desc[it + 2]);
+        int e_next = 0;
+        if constexpr (EXACT) {
+          if (has1) e_next = exact_v_exponent(sm, staged_magnitude<D, ST, SCALED>(tn1, st), tn1.is_int8, wave, lane);
+        }
         const bool compute = (t.wmask >> wave) & 1;
         auto ride = [&](int i) {
           if (has2 && i % STRIDE == 0 && i / STRIDE < NPART)
@@ -891,11 +1076,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         auto none = [&]() {};
         if (!lagging) {
           const bool dma = has1 && k_wave && !tn1.is_int8;
-          if (has1) commit_tile<D, ST, SCALED>(p, tn1, st, sm, knext, vnext);
+          if (has1) commit_tile<D, ST, SCALED>(p, tn1, st, sm, knext, vnext, e_next, i8_min_scale);
           if (compute) {
-            lead_tile_scaled<D, SCALED, GENERAL, ST, PF_PV>(p, t, tn1, head, ws, sm.k[kbuf], sm.ksc[kbuf],
-                                                            sm.v[vbuf], sm.k[knext], dma, plan,
-                                                            k_lane, v_lane, r, hh, my_qb, qb_lo, n_qbt, pb, ride);
+            lead_tile_scaled<D, SCALED, GENERAL, EXACT, ST, PF_PV>(p, t, tn1, head, ws, sm.k[kbuf], sm.ksc[kbuf],
+                                                                   sm.v[vbuf], sm.k[knext], dma, plan,
+                                                                   k_lane, v_lane, r, hh, my_qb, qb_lo, n_qbt, pb,
+                                                                   ride, e_cur);
           } else {
             if (dma) issue_kdma<D, ST>(p, tn1, head, sm, knext, plan);
             if (has2) issue_stage<D, ST, SCALED>(p, tn2, head, st, plan);
@@ -903,10 +1089,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         } else {
           if (pending) pv_tile<D, PF_PV>(ws, sm.v[vprev], v_lane, pb);
           pending = false;
-          if (has1) commit_tile<D, ST, SCALED>(p, tn1, st, sm, knext, vnext);
+          if (has1) commit_tile<D, ST, SCALED>(p, tn1, st, sm, knext, vnext, e_next, i8_min_scale);
           if (compute) {
-            qk_softmax<D, SCALED, GENERAL>(p, t, ws, sm.k[kbuf], sm.ksc[kbuf], k_lane, r, hh, my_qb,
-                                           qb_lo, n_qbt, pb, ride, none);
+            qk_softmax<D, SCALED, GENERAL, EXACT>(p, t, ws, sm.k[kbuf], sm.ksc[kbuf], k_lane, r, hh, my_qb,
+                                                  qb_lo, n_qbt, pb, e_cur, ride, none);
             pending = true;
           } else if (has2) {
             issue_stage<D, ST, SCALED>(p, tn2, head, st, plan);
@@ -919,9 +1105,54 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         vbuf = vnext;
         tc = tn1;
         tn1 = tn2;
+        e_cur = e_next;
       }
       // the last tile's V buffer stays untouched until the next pass's barriers
       if (pending) pv_tile<D, PF_PV>(ws, sm.v[vprev], v_lane, pb);
+    }
+  }
+  };
+
+  all_passes(std::integral_constant<bool, false>());
+  // ---- check of the fast form, per query row of this wave: its output
+  // (o / l) must be finite and, where the row sees a key, reach 2^-12 in its
+  // largest column (then the 2^-25 that a bf16 V element below 2^-17 may lose
+  // in fp16 stays below 2^-13 of the row's largest output); no int8 row scale
+  // may have been an fp16 subnormal. If any wave's check fails, the whole
+  // workgroup runs again in the exact form.
+  {
+    float omax = 0.f;
+#pragma unroll
+    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+      for (int e2 = 0; e2 < 16; ++e2) omax = fmaxf(omax, fabsf(ws.o[i][e2]));
+    omax = swap_halves_max(omax);
+    const float l_tot = swap_halves_sum(ws.l_run);
+    const bool sees = ws.seen && l_tot > 0.f;
+    float osum = 0.f;   // a sum keeps NaN and infinity, which fmaxf would drop
+#pragma unroll
+    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+      for (int e2 = 0; e2 < 16; ++e2) osum += fabsf(ws.o[i][e2]);
+    const bool o_finite = __builtin_isfinite(osum);
+    const bool fail = i8_min_scale < 0x1p-14f || (q_ok && sees && (!o_finite || omax < 0x1p-12f * l_tot));
+    const bool any_fail = __ballot(fail) != 0;
+    if (lane == 0) sm.wave_count[wave] = any_fail ? 1 : 0;
+    __syncthreads();
+    int redo = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) redo |= sm.wave_count[w];
+    __syncthreads();
+    if (redo) {
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int e2 = 0; e2 < 16; ++e2) ws.o[i][e2] = 0.f;
+      ws.m_run = -INFINITY;
+      ws.l_run = 0.f;
+      ws.seen = !GENERAL;
+      ws.e_o = 0;
+      all_passes(std::integral_constant<bool, true>());
     }
   }
 
@@ -929,6 +1160,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   const float l_tot = swap_halves_sum(ws.l_run);
   const bool any = ws.seen && l_tot > 0.f;
   const float inv = any ? 1.0f / l_tot : 0.f;
+  // o holds O * 2^e_o: each o / l is scaled by 2^-e_o (exact)
+  const int esh = -ws.e_o;
   // partial form and pieces of split units: normalised O in fp32, merged
   // later without another rounding
   float* const of32 = slot >= 0 ? p.ws_o + ((int64_t)slot * BQ + (q_row - q_lo)) * D
@@ -942,8 +1175,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<float4*>(op + dt * 32 + 8 * g + 4 * hh) =
-            make_float4(any ? ws.o[dt][4 * g + 0] * inv : 0.0f, any ? ws.o[dt][4 * g + 1] * inv : 0.0f,
-                        any ? ws.o[dt][4 * g + 2] * inv : 0.0f, any ? ws.o[dt][4 * g + 3] * inv : 0.0f);
+            make_float4(any ? ldexpf(ws.o[dt][4 * g + 0] * inv, esh) : 0.0f, any ? ldexpf(ws.o[dt][4 * g + 1] * inv, esh) : 0.0f,
+                        any ? ldexpf(ws.o[dt][4 * g + 2] * inv, esh) : 0.0f, any ? ldexpf(ws.o[dt][4 * g + 3] * inv, esh) : 0.0f);
   } else if (q_ok) {
     uint16_t* op = p.out + ((int64_t)q_row * p.n_heads + head) * D;
 #pragma unroll
@@ -952,10 +1185,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       for (int g = 0; g < 4; ++g) {
         const int d = dt * 32 + 8 * g + 4 * hh;
         // rows without a visible key store +0 (o * 0 could give -0)
-        const __bf16 v0 = (__bf16)(any ? ws.o[dt][4 * g + 0] * inv : 0.0f);
-        const __bf16 v1 = (__bf16)(any ? ws.o[dt][4 * g + 1] * inv : 0.0f);
-        const __bf16 v2 = (__bf16)(any ? ws.o[dt][4 * g + 2] * inv : 0.0f);
-        const __bf16 v3 = (__bf16)(any ? ws.o[dt][4 * g + 3] * inv : 0.0f);
+        const __bf16 v0 = (__bf16)(any ? ldexpf(ws.o[dt][4 * g + 0] * inv, esh) : 0.0f);
+        const __bf16 v1 = (__bf16)(any ? ldexpf(ws.o[dt][4 * g + 1] * inv, esh) : 0.0f);
+        const __bf16 v2 = (__bf16)(any ? ldexpf(ws.o[dt][4 * g + 2] * inv, esh) : 0.0f);
+        const __bf16 v3 = (__bf16)(any ? ldexpf(ws.o[dt][4 * g + 3] * inv, esh) : 0.0f);
         const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
         const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
         *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);

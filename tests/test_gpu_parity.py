@@ -1,11 +1,16 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle.
 
 Bars: int8 codes and fp32 scales bit-exact; qknorm_rope3d within one bf16
-ulp of the oracle's single rounding; attention within max-abs 4e-3 and
-relative RMS 1e-2 of the unrounded fp64 result, LSE within 1e-3.
-Small cases are compared element by element; the full-size workloads run in
-the same launch configuration as the benchmark and are compared on sampled
-query rows (every head, first/last/ragged q-tiles)."""
+ulp of the oracle's single rounding (at least 99.9% bit-identical);
+attention within relative RMS 1e-2 of the unrounded fp64 result and, element
+by element, within max-abs 4e-3 where |ref| < 1 (a correctly rounded bf16
+output is then within 2e-3) and within 4e-3 beyond half a bf16 ulp of ref
+above that (where the output's own rounding alone may exceed 4e-3); LSE
+within 1e-3. Small cases are compared element by element; the full-size
+workloads run in the same launch configuration as the benchmark and are
+compared on every row of two whole heads (one of them holding units that the
+balanced launch cuts) and on sampled query rows of every head
+(first/last/ragged q-tiles)."""
 import numpy as np
 import pytest
 
@@ -318,7 +323,7 @@ def test_dense_block_mask_matches_sdpa_within_the_pages_figure():
     out, _ = run_attn(q, [{"k": k, "v": v, "dtype": "bf16"}], mask, 128, 128)
     t = [torch.from_numpy(oracle.bf16_to_f64(a)).permute(1, 0, 2) for a in (q, k, v)]
     ref = torch.nn.functional.scaled_dot_product_attention(*t).permute(1, 0, 2).numpy()
-    max_abs, rrms, beyond = attn_errors(out, ref)
+    max_abs, rrms, beyond, _ = attn_errors(out, ref)
     _say(f"   dense vs SDPA: max-abs {max_abs:.2e}, beyond half an ulp {beyond:.2e}, page {fx['bf16_max_abs_error']}")
     assert beyond <= fx["bf16_max_abs_error"]
     assert rrms <= 1e-2
@@ -412,7 +417,8 @@ def test_full_size_hot_path_sampled(name):
     """The benchmark's step at full size: [qknorm_rope3d] -> [kv_quant_int8 of the
     cache] -> attention on the GPU, both through attn_fwd and through
     attn_fwd_balanced with the library's plan (the benchmark's launch); the
-    oracle runs the same chain on the CPU and computes the sampled rows."""
+    oracle runs the same chain on the CPU and computes the sampled rows of
+    every head and every row of two whole heads."""
     import torch
     import streaming_video_dit_amd as sdit
     cfg = W.WORKLOADS[name]
@@ -458,6 +464,16 @@ def test_full_size_hot_path_sampled(name):
     _say(f"   {len(rows)} rows x {H} heads: max-abs {e[0]:.2e} ({e[2]:.2e} beyond half an ulp), rel-RMS {e[1]:.2e}")
     e = assert_attn_close(out_b[rows], lse_b[:, rows], O, LSE, name + " balanced")
     _say(f"   balanced: max-abs {e[0]:.2e} ({e[2]:.2e} beyond half an ulp), rel-RMS {e[1]:.2e}")
+    # every row of two whole heads: head 0 and the head of XCD 0's last work
+    # unit, which the balanced launch cuts into pieces whenever it cuts at all
+    osegs = segments_for_oracle(inp, rk, ref_quant)
+    n_qt = -(-n_q // 256)
+    heads = sorted({0, min(H - 1, ((H * n_qt) // 8 - 1) // n_qt)})
+    Of, LSEf = oracle.attention(rq, osegs, inp.mask, cfg.block, cfg.block, heads=heads)
+    for o_x, l_x, label in ((out, lse, name), (out_b, lse_b, name + " balanced")):
+        e = assert_attn_close(o_x[:, heads], l_x[heads], Of, LSEf, f"{label}, heads {heads}")
+        _say(f"   {label}: every row of heads {heads}: max-abs {e[0]:.2e} ({e[2]:.2e} beyond half an ulp), "
+             f"rel-RMS {e[1]:.2e}")
     # every row, every head: finite output, and LSE finite where a key is visible
     assert np.all((out & 0x7F80) != 0x7F80)
     assert np.all((out_b & 0x7F80) != 0x7F80)

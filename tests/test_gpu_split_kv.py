@@ -3,8 +3,8 @@ with the fp64 oracle, through the C ABI.
 
   * the fp32 partial output over a group of segments against the oracle's
     attention over that group, with the bars of the bf16 output it becomes
-    (4e-3 beyond half a bf16 ulp, relative RMS 1e-2, LSE 1e-3; rows that see
-    nothing: exact 0 and -inf);
+    (max-abs 4e-3 where |ref| < 1, else 4e-3 beyond half a bf16 ulp;
+    relative RMS 1e-2; LSE 1e-3; rows that see nothing: exact 0 and -inf);
   * the merge alone, fed the oracle's partials in fp32, against the oracle's
     merge of the same fp32 values: within one bf16 ulp, LSE within 1e-5;
   * the whole split path (partials on the GPU, merge on the GPU) against the
@@ -14,8 +14,8 @@ import numpy as np
 import pytest
 
 import workloads as W
-from helpers import ATOL_LSE, ATOL_O, RRMS_O, assert_attn_close, bf16_to_float, dev, gpu_segments, half_ulp_bf16, \
-    host_u16, run_attn
+from helpers import ATOL_LSE, ATOL_O, RRMS_O, assert_attn_close, attn_tolerance, bf16_to_float, dev, gpu_segments, \
+    half_ulp_bf16, host_u16, run_attn
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -99,8 +99,8 @@ def _assert_partial_close(O, L, O_ref, L_ref, what):
     assert np.all(O[empty_rows] == 0), what
     # the fp32 partial is an intermediate of a bf16 result: same bar as the bf16 output
     diff = O - O_ref
-    beyond = float((np.abs(diff) - half_ulp_bf16(O_ref)).max())
-    assert beyond <= ATOL_O, f"{what}: error {beyond:.3e} beyond half a bf16 ulp (max-abs {np.abs(diff).max():.3e})"
+    worst = float((np.abs(diff) / attn_tolerance(O_ref)).max())
+    assert worst <= 1.0, f"{what}: error {worst:.3f} x the per-element bar (max-abs {np.abs(diff).max():.3e})"
     denom = float(np.sqrt((O_ref ** 2).sum()))
     if denom > 0:
         assert float(np.sqrt((diff ** 2).sum())) / denom <= RRMS_O, what

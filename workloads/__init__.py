@@ -45,18 +45,26 @@ def _f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
 
 
 def normal_bf16(seed: int, tid: int, shape, outlier_p: float = 0.0,
-                outlier_mult: float = 8.0, outlier_tid: Optional[int] = None) -> np.ndarray:
-    """N(0,1) samples as bf16 bits. With ``outlier_p`` > 0 each element is,
-    independently, multiplied by ``outlier_mult`` with that probability (the
-    multiplication by a power of two happens before the bf16 rounding and is
-    exact)."""
+                outlier_mult: float = 8.0, outlier_tid: Optional[int] = None, sigma: float = 1.0) -> np.ndarray:
+    """N(0, sigma^2) samples as bf16 bits (sigma scales the fp64 draw before
+    the roundings). With ``outlier_p`` > 0 each element is, independently,
+    multiplied by ``outlier_mult`` with that probability (the multiplication
+    by a power of two happens before the bf16 rounding and is exact)."""
     rng = np.random.default_rng([seed, tid])
-    x = rng.standard_normal(size=shape)
+    x = rng.standard_normal(size=shape) * sigma
     if outlier_p > 0.0:
         assert outlier_tid is not None
         orng = np.random.default_rng([seed, outlier_tid])
         hit = orng.random(size=shape) < outlier_p
         x = np.where(hit, x * outlier_mult, x)
+    return _f32_to_bf16_bits(x.astype(np.float32))
+
+
+def signed_uniform_bf16(seed: int, tid: int, shape, lo: float, hi: float) -> np.ndarray:
+    """Magnitudes U(lo, hi) with random signs, as bf16 bits (rounded through
+    fp32; choose hi so that the rounding stays below any limit of interest)."""
+    rng = np.random.default_rng([seed, tid])
+    x = rng.uniform(lo, hi, size=shape) * np.where(rng.random(size=shape) < 0.5, -1.0, 1.0)
     return _f32_to_bf16_bits(x.astype(np.float32))
 
 
