@@ -195,6 +195,26 @@ int sdit_attn_fwd_balanced(const void* q, int32_t n_q,
                            void* out, float* lse, void* workspace, int64_t workspace_bytes,
                            int32_t split_tile, void* stream);
 
+/* sdit_attn_fwd_balanced for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same computation, arguments and plan as sdit_attn_fwd_balanced
+ * without the workspace: the pieces' partials go to a device array the
+ * library owns, SDIT_STATIC_SCRATCH_BYTES (64 MiB) per GPU, held from the
+ * library's first use on that GPU until the process ends. That covers the
+ * largest plan at head_dim 128; a plan that needed more would be rejected
+ * with SDIT_ERR_INVALID before anything is launched. The call allocates
+ * nothing and calls no allocating routine. Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (different streams, or
+ * graph replays running concurrently) race and must be ordered by the
+ * caller. Nothing in the array has to start at any value (each call writes
+ * every entry it later reads). */
+#define SDIT_STATIC_SCRATCH_BYTES ((int64_t)64 << 20)
+int sdit_attn_fwd_balanced_static(const void* q, int32_t n_q,
+                                  const sdit_kv_segment* segs, int32_t n_segs,
+                                  const uint8_t* block_mask, int32_t block_q, int32_t block_k,
+                                  int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                  void* out, float* lse, int32_t split_tile, void* stream);
+
 /* Partial attention for a split of the keys (split-KV): the computation of
  * sdit_attn_fwd over the given segments, with O written normalised in fp32
  * so that results over disjoint key sets combine without another rounding

@@ -66,6 +66,7 @@ def load_library(path: str) -> ctypes.CDLL:
     _i64 = ctypes.c_int64
     L.sdit_attn_fwd_balanced.argtypes = L.sdit_attn_fwd.argtypes[:-1] + [_vp, _i64, _i32, _vp]
     L.sdit_validate_attn_balanced_args.argtypes = L.sdit_validate_attn_args.argtypes + [_vp, _i64, _i32]
+    L.sdit_attn_fwd_balanced_static.argtypes = L.sdit_attn_fwd.argtypes[:-1] + [_i32, _vp]
     _pi32 = ctypes.POINTER(ctypes.c_int32)
     L.sdit_attn_balanced_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _pi32, _pi32]
     _pp = ctypes.POINTER(ctypes.c_void_p)
@@ -83,7 +84,7 @@ def load_library(path: str) -> ctypes.CDLL:
               "sdit_validate_kv_quant_args", "sdit_attn_fwd", "sdit_validate_attn_args",
               "sdit_attn_fwd_partial", "sdit_validate_attn_partial_args", "sdit_attn_merge",
               "sdit_validate_attn_merge_args", "sdit_attn_fwd_balanced", "sdit_validate_attn_balanced_args",
-              "sdit_attn_balanced_plan"):
+              "sdit_attn_balanced_plan", "sdit_attn_fwd_balanced_static"):
         getattr(L, n).restype = ctypes.c_int
     if L.sdit_abi_version() != ABI_VERSION:
         raise ImportError(f"{path} ABI {L.sdit_abi_version()} != binding ABI {ABI_VERSION}")
@@ -211,6 +212,17 @@ def attn_fwd_balanced(q, n_q: int, segs, block_mask, block_q: int, block_k: int,
     _check(L.sdit_attn_fwd_balanced(_ptr(q), n_q, arr, len(segs), _ptr(block_mask), block_q, block_k, n_heads,
                                     head_dim, softmax_scale, _ptr(out), _ptr(lse), _ptr(workspace),
                                     workspace_bytes, split_tile, _stream(stream)))
+
+
+def attn_fwd_balanced_static(q, n_q: int, segs, block_mask, block_q: int, block_k: int, n_heads: int,
+                             head_dim: int, out, lse=None, softmax_scale: float = 0.0, split_tile: int = -1,
+                             stream=None) -> None:
+    """sdit_attn_fwd_balanced_static: the balanced launch with the library's
+    own device scratch (no workspace argument, nothing allocated)."""
+    arr = segs if isinstance(segs, ctypes.Array) else make_segments(segs)
+    _check(lib().sdit_attn_fwd_balanced_static(_ptr(q), n_q, arr, len(segs), _ptr(block_mask), block_q, block_k,
+                                               n_heads, head_dim, softmax_scale, _ptr(out), _ptr(lse), split_tile,
+                                               _stream(stream)))
 
 
 def attn_balanced_plan(n_q: int, n_heads: int, n_tiles: int, n_cus: int, split_tile: int = -1):

@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libsdit.so")
 LIB_SINGLE_STAGE = os.path.join(HERE, "libsdit_single_stage.so")
 
 SOURCES = ["sdit_api.cpp", "qknorm_rope3d.hip", "kv_quant_int8.hip", "attn_fwd.hip", "attn_merge.hip", "window_permute.hip",
-           "norms.hip"]
+           "norms.hip", "static_scratch.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",

@@ -665,6 +665,35 @@ SDIT_API int sdit_validate_attn_balanced_args(const void* q, int32_t n_q, const 
                          workspace_bytes, split_tile);
 }
 
+namespace {
+
+// The balanced launch with the workspace at ws (ws_bytes at least what its
+// plan uses): attention kernel, then the merge of the cut pieces.
+int launch_balanced(sdit::AttnParams& P, int head_dim, int32_t split_tile, void* ws, int64_t ws_bytes, void* out,
+                    float* lse, hipStream_t stream, const char* fn) {
+  int C = 1;
+  if (split_tile != 0) {
+    const int st = cu_per_xcd(&C);
+    if (st != SDIT_OK) return st;
+  }
+  const BalancedPlan bp = plan_balanced(P.n_qt * P.n_heads, P.n_tiles, C, split_tile);
+  const int64_t need = (ws_o_floats(bp.rmax, head_dim) + (int64_t)sdit::kNumXcd * bp.rmax * 2 * sdit::kAttnBQ) * 4;
+  if (need > ws_bytes)
+    return fail(SDIT_ERR_INVALID, "%s: the cut needs %lld bytes of scratch, %lld available", fn, (long long)need,
+                (long long)ws_bytes);
+  P.split_tile = bp.tile;
+  P.split_rmax = bp.rmax;
+  P.grid = bp.grid;
+  P.cu_per_xcd = C;
+  P.ws_o = (float*)ws;
+  P.ws_lse = P.ws_o + ws_o_floats(P.split_rmax, head_dim);
+  int st = device_status(sdit::launch_attn_fwd(P, head_dim, stream), fn);
+  if (st != SDIT_OK) return st;
+  return device_status(sdit::launch_attn_split_merge(P, (uint16_t*)out, lse, head_dim, stream), fn);
+}
+
+}  // namespace
+
 SDIT_API int sdit_attn_fwd_balanced(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs,
                                     const uint8_t* block_mask, int32_t block_q, int32_t block_k, int32_t n_heads,
                                     int32_t head_dim, float softmax_scale, void* out, float* lse, void* workspace,
@@ -677,20 +706,28 @@ SDIT_API int sdit_attn_fwd_balanced(const void* q, int32_t n_q, const sdit_kv_se
                        workspace_bytes, split_tile);
   if (st != SDIT_OK) return st;
   if (n_q == 0) return ok();
-  int C = 1;
-  if (split_tile != 0) {
-    st = cu_per_xcd(&C);
-    if (st != SDIT_OK) return st;
-  }
-  const BalancedPlan bp = plan_balanced(P.n_qt * P.n_heads, P.n_tiles, C, split_tile);
-  P.split_tile = bp.tile;
-  P.split_rmax = bp.rmax;
-  P.grid = bp.grid;
-  P.cu_per_xcd = C;
-  P.ws_o = (float*)workspace;
-  P.ws_lse = P.ws_o + ws_o_floats(P.split_rmax, head_dim);
-  st = device_status(sdit::launch_attn_fwd(P, head_dim, (hipStream_t)stream), "attn_fwd_balanced");
-  if (st != SDIT_OK) return st;
-  return device_status(sdit::launch_attn_split_merge(P, (uint16_t*)out, lse, head_dim, (hipStream_t)stream),
-                       "attn_fwd_balanced (merge)");
+  return launch_balanced(P, head_dim, split_tile, workspace, workspace_bytes, out, lse, (hipStream_t)stream,
+                         "attn_fwd_balanced");
 }
+
+SDIT_API int sdit_attn_fwd_balanced_static(const void* q, int32_t n_q, const sdit_kv_segment* segs, int32_t n_segs,
+                                           const uint8_t* block_mask, int32_t block_q, int32_t block_k,
+                                           int32_t n_heads, int32_t head_dim, float softmax_scale, void* out,
+                                           float* lse, int32_t split_tile, void* stream) {
+  sdit::AttnParams P;
+  int st = fill_attn_params(q, n_q, segs, n_segs, block_mask, block_q, block_k, n_heads, head_dim, softmax_scale,
+                            out, lse, &P);
+  if (st != SDIT_OK) return st;
+  if (split_tile < -1 || (split_tile > 0 && split_tile >= P.n_tiles))
+    return fail(SDIT_ERR_INVALID, "attn_fwd_balanced_static: split_tile %d not -1, 0 or in [1, %d)", split_tile,
+                P.n_tiles);
+  if (n_q == 0) return ok();
+  void* ws = nullptr;
+  const hipError_t e = sdit::static_scratch(&ws);
+  if (e != hipSuccess) return device_status(e, "attn_fwd_balanced_static (scratch address)");
+  return launch_balanced(P, head_dim, split_tile, ws, SDIT_STATIC_SCRATCH_BYTES, out, lse, (hipStream_t)stream,
+                         "attn_fwd_balanced_static");
+}
+
+static_assert(SDIT_STATIC_SCRATCH_BYTES == sdit::kStaticScratchBytes, "static scratch size");
+static_assert(SDIT_STATIC_SCRATCH_BYTES >= SDIT_ATTN_WORKSPACE_BYTES(128), "static scratch covers every plan");

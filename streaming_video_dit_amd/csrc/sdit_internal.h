@@ -126,6 +126,12 @@ __host__ __device__ inline XcdUnits xcd_units(int32_t n_units, int32_t xcd, int3
   return u;
 }
 
+// Library-owned device scratch of the allocation-free balanced attention
+// (static_scratch.hip): its device address on the current device, looked up
+// once per device.
+constexpr int64_t kStaticScratchBytes = (int64_t)64 << 20;
+hipError_t static_scratch(void** ptr);
+
 // ---------------------------------------------------------------- attn_merge
 constexpr int kMaxMergeParts = 8;
 struct MergeParams {
