@@ -31,6 +31,16 @@ with HIP events around each launch on the stream it runs on.
 The attention time covers both launches of the balanced call.
 ``cpu_baseline`` times the fp64 oracle on the host (heads processed one by
 one until about 10 s have elapsed, scaled to TFLOP/s).
+
+By default the line also carries a ``configs`` object with one record per
+main workload (tiny, Wan chunk, Wan chunk with an int8 cache, Large-DiT,
+block-sparse SR), each timed the same way after the headline workload:
+attention ms (mean, median, p10-p90), step ms, effective TFLOP/s and the
+fraction of the bf16 peak (the tiny one, which is launch-latency bound,
+against its algorithmic bytes instead), HBM traffic where a profile of the
+current kernel sources exists, and the oracle's seconds on a bounded sample.
+``clocks`` holds the engine and memory clock levels read before and after
+the timed work.
 """
 from __future__ import annotations
 
@@ -51,6 +61,9 @@ import workloads as W  # noqa: E402
 METRIC = "attention ms/layer/chunk + effective TFLOP/s (% bf16 MFMA peak), 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# Q.K^T runs as a bf16 MFMA; P.V multiplies fp16 probabilities with V staged
+# in fp16 (same MFMA rate, 3 more mantissa bits for P); accumulation fp32.
+DTYPE = "bf16 (P.V in fp16)"
 
 
 def _dev(a, torch):
@@ -170,6 +183,37 @@ class Step:
             ev_after.record()
         if cfg.window:
             sdit.window_permute(self.out_w, self.out, cfg.T, cfg.Hl, cfg.Wl, H, d, cfg.window, inverse=True)
+
+
+def attn_algorithmic_bytes(cfg: W.Config, mask) -> int:
+    """One pass over every operand of one attention call: q, each segment's K
+    and V (int8 codes plus their fp32 scales, or bf16), the bf16 output, the
+    fp32 LSE and the mask."""
+    H, d, n = cfg.n_heads, cfg.head_dim, cfg.n_q
+    b = 2 * n * H * d * 2 + 4 * H * n + int(np.asarray(mask).size)
+    for L, i8 in zip(cfg.seg_lens, cfg.seg_int8):
+        b += 2 * L * H * d * (1 if i8 else 2) + (2 * L * H * 4 if i8 else 0)
+    return b
+
+
+def read_clocks():
+    """Current engine (sclk) and memory (mclk) clock levels in MHz from the
+    driver's sysfs files (the line marked '*'), or None where unreadable."""
+    import glob
+    out = {}
+    for key in ("sclk", "mclk"):
+        val = None
+        for f in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{key}")):
+            try:
+                for line in open(f):
+                    if line.rstrip().endswith("*"):
+                        val = int("".join(ch for ch in line.split(":", 1)[1] if ch.isdigit()))
+            except (OSError, ValueError, IndexError):
+                continue
+            if val is not None:
+                break
+        out[key + "_mhz"] = val
+    return out
 
 
 def device_info(torch):
@@ -359,9 +403,68 @@ def cpu_baseline(cfg: W.Config, budget_s: float = 10.0):
     flops = W.attn_flops(cfg, inp.mask) * heads / cfg.n_heads
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": el,
-            "sample": f"{cfg.name}: qknorm_rope3d of the whole chunk"
-                      f"{' + int8 quantisation of the cache' if any(cfg.seg_int8) else ''}"
-                      f" + attention for {heads} of {cfg.n_heads} heads, fp64 numpy, {el:.1f} s"}
+            "sample": f"{cfg.name}: " + " + ".join(
+                (["qknorm_rope3d of the whole chunk"] if cfg.rope else [])
+                + (["int8 quantisation of the cache"] if any(cfg.seg_int8) else [])
+                + [f"attention for {heads} of {cfg.n_heads} heads"]) + f", fp64 numpy, {el:.1f} s"}
+
+
+def time_step(step: "Step", torch, steps: int, warmup: int, with_merge: bool = False):
+    """W untimed steps, then K steps bracketed by events; per-step attention
+    events on the launch stream. Returns (ms per step, attention ms per call
+    list, events, wall seconds)."""
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3 if with_merge else 2)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        step.run(*evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    return start.elapsed_time(end) / steps, [e[0].elapsed_time(e[1]) for e in evs], evs, t_wall
+
+
+def config_record(cfg: W.Config, torch, sdit, steps: int, warmup: int, cpu_budget: float, step=None, timing=None,
+                  cpu=None):
+    """One workload's record for the ``configs`` object: the balanced
+    attention call of the library's plan inside the full step (``step`` and
+    ``timing`` reuse the headline measurement, ``cpu`` its oracle timing)."""
+    if step is None:
+        step = Step(cfg, torch, sdit)
+    ms_step, attn_ms, _, _ = timing if timing is not None else time_step(step, torch, steps, warmup)
+    a = np.asarray(attn_ms)
+    med = float(np.median(a))
+    rec = {"description": cfg.description, "n_heads": cfg.n_heads, "head_dim": cfg.head_dim, "n_q": cfg.n_q,
+           "segments": cfg.seg_lens, "int8_segments": cfg.seg_int8, "block": cfg.block,
+           "kept_tiles": int(step.inp.mask.sum()), "mask_tiles": int(step.inp.mask.size),
+           "effective_gflop": round(step.flops / 1e9, 6), "cut_at_tile": step.plan[0],
+           "attn_workgroups": step.plan[1],
+           "attn_ms": round(float(a.mean()), 5), "attn_ms_median": round(med, 5),
+           "attn_ms_p10_p90": [round(float(np.percentile(a, 10)), 5), round(float(np.percentile(a, 90)), 5)],
+           "step_ms": round(ms_step, 5)}
+    tflops = step.flops / (float(a.mean()) * 1e-3) / 1e12
+    nbytes = attn_algorithmic_bytes(cfg, step.inp.mask)
+    rec["tflops"] = round(tflops, 3)
+    rec["pct_bf16_peak"] = round(100 * tflops / PEAK_BF16_TFLOPS, 2)
+    if cfg.name == "tiny":
+        gbs = nbytes / (float(a.mean()) * 1e-3) / 1e9
+        rec["roofline"] = {"bound": "latency", "achieved": round(gbs, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(gbs / PEAK_HBM_GBS, 6), "algorithmic_bytes": nbytes,
+                           "traffic": measured_traffic(cfg.name)}
+    else:
+        rec["roofline"] = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "algorithmic_bytes": nbytes,
+                           "traffic": measured_traffic(cfg.name)}
+    if cpu is not None or cpu_budget > 0:
+        cb = cpu if cpu is not None else cpu_baseline(cfg, cpu_budget)
+        rec["cpu_baseline"] = {"seconds": round(cb["seconds"], 3), "value": cb["value"], "unit": cb["unit"],
+                               "cores": cb["cores"], "sample": cb["sample"]}
+    return rec
 
 
 def main():
@@ -384,6 +487,11 @@ def main():
                     help="also time RMSNorm and LayerNorm + modulate on the workload's hidden-state shape")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (calibrates HBM byte counters)")
+    ap.add_argument("--configs", default=",".join(W.WORKLOAD_ORDER),
+                    help="comma-separated workloads timed after the headline one for the 'configs' object "
+                         "('none' to skip)")
+    ap.add_argument("--config-cpu-budget", type=float, default=3.0,
+                    help="seconds of oracle time per entry of the 'configs' object (0: none)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -409,6 +517,7 @@ def main():
         return
 
     cfg = W.WORKLOADS[args.workload]
+    clocks = {"before": read_clocks()}
     step = Step(cfg, torch, sdit, args.kv_parts, args.launch, args.split_tile)
     for _ in range(args.warmup):
         step.run()
@@ -420,19 +529,9 @@ def main():
     torch.cuda.synchronize()
     h2 = hashlib.md5(step.out.cpu().numpy().tobytes()).hexdigest()
 
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3 if args.kv_parts > 1 else 2))
-           for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        step.run(*evs[i])
-    end.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_step = start.elapsed_time(end) / args.steps
-    attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    timing = time_step(step, torch, args.steps, 0, with_merge=args.kv_parts > 1)
+    ms_step, attn_ms, evs, t_wall = timing
+    clocks["after"] = read_clocks()
     attn_avg = float(np.mean(attn_ms))
     value = step.flops / (ms_step * 1e-3) / 1e12
     attn_tflops = step.flops / (attn_avg * 1e-3) / 1e12
@@ -448,7 +547,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": cfg.name, "description": cfg.description, "n_heads": cfg.n_heads,
                    "head_dim": cfg.head_dim, "n_q": cfg.n_q, "segments": cfg.seg_lens,
@@ -464,6 +563,7 @@ def main():
         "pct_bf16_peak_attn": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "deterministic": h1 == h2,
         "device": device_info(torch),
+        "clocks": clocks,
         "wall_s_timed": round(t_wall, 3),
         "roofline": {"kernel": (f"attn_fwd_kernel<{cfg.head_dim}>"
                                + (f" + attn_split_merge_kernel<{cfg.head_dim}>" if step.plan[0] > 0 else "")),
@@ -485,6 +585,21 @@ def main():
         rec["norms"] = measure_norms(cfg, torch, sdit, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+    names = [] if args.configs in ("", "none") else [n for n in args.configs.split(",") if n]
+    if names:
+        configs = {}
+        headline_plain = args.kv_parts == 1 and args.launch == "balanced" and args.split_tile == -1
+        cpu_budget = 0.0 if args.no_cpu_baseline else args.config_cpu_budget
+        for name in names:
+            if name == cfg.name and headline_plain:
+                configs[name] = config_record(cfg, torch, sdit, args.steps, args.warmup, cpu_budget, step=step,
+                                              timing=timing, cpu=rec.get("cpu_baseline"))
+            else:
+                c = W.WORKLOADS[name]
+                configs[name] = config_record(c, torch, sdit, args.steps, args.warmup, cpu_budget)
+                torch.cuda.empty_cache()
+        rec["configs"] = configs
+        rec["clocks"]["after_configs"] = read_clocks()
     print(json.dumps(rec), flush=True)
 
 

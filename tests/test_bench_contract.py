@@ -44,7 +44,8 @@ def test_bench_prints_one_contract_line():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1",
-                        "--no-cpu-baseline"], capture_output=True, text=True, cwd=ROOT, timeout=300)
+                        "--no-cpu-baseline", "--configs", "tiny,wan13b,bsa_sr"], capture_output=True, text=True,
+                       cwd=ROOT, timeout=300)
     assert p.returncode == 0, p.stderr[-2000:]
     lines = [l for l in p.stdout.splitlines() if l.strip()]
     assert len(lines) == 1
@@ -53,9 +54,17 @@ def test_bench_prints_one_contract_line():
               "vs_baseline", "dtype", "data", "config", "roofline"):
         assert k in r, k
     assert r["n_gpus"] == 1 and r["steps"] == 3 and r["warmup"] == 1
-    assert r["higher_is_better"] is True and r["data"] == "synthetic" and r["dtype"] == "bf16"
+    assert r["higher_is_better"] is True and r["data"] == "synthetic" and r["dtype"].startswith("bf16")
     assert r["config"]["workload"] == "wan13b" and r["value"] > 0 and r["ms_per_step"] > 0
     rf = r["roofline"]
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 2500.0
     assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], abs=1e-4)
     assert rf["traffic"] is None or rf["traffic"] > 0
+    # one record per requested workload; the headline one is the same measurement
+    assert sorted(r["configs"]) == ["bsa_sr", "tiny", "wan13b"]
+    assert r["configs"]["wan13b"]["attn_ms"] == r["attn_ms"]
+    for name, c in r["configs"].items():
+        assert c["attn_ms"] > 0 and c["step_ms"] >= c["attn_ms_p10_p90"][0] * 0.5
+        assert c["roofline"]["bound"] == ("latency" if name == "tiny" else "mfma")
+        assert c["roofline"]["frac"] > 0
+    assert set(r["clocks"]) >= {"before", "after"}
