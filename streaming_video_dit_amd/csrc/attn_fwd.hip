@@ -173,6 +173,9 @@ struct Smem {
   uint16_t v[NVBUF][BK * Layout<D>::VS];  // fp16, padded rows
   float ksc[2][BK];                       // scaled path: per-key multiplier of the raw score
   uint2 desc[LIST_CAP];                   // kept tiles of the current pass (pack_desc)
+  // fine masks: per listed tile, bit 16 j + s = mask[first q-block + s][first
+  // k-block of the tile + j] (up to 16 q-blocks of the rows, 4 k-blocks of a tile)
+  uint64_t kbits[LIST_CAP];
   int32_t wave_count[NW];
   float vmax[NW];   // every wave's largest staged V magnitude (exact form)
 };
@@ -207,6 +210,7 @@ struct TileRef {
   int is_int8;
   int kb_start;
   int wmask;   // waves with a kept (q-block, k-block) pair in the tile
+  uint64_t kbits;  // fine masks only: the tile's (q-block, k-block) keep bits (Smem::kbits)
 };
 
 // descriptor: x = first key inside the segment, y = segment | n_valid << 8 | wave mask << 16
@@ -231,6 +235,21 @@ __device__ __forceinline__ TileRef tile_ref(const AttnParams& p, uint2 d) {
   // complete the scalar loads here, before the step's LDS traffic starts
   // (their wait would otherwise also wait for every LDS read in flight)
   asm volatile("" ::"s"(t.k), "s"(t.v), "s"(t.k_scale), "s"(t.v_scale), "s"(t.is_int8), "s"(t.kb_start));
+  return t;
+}
+
+// Listed tile i (fine masks: with its keep bits).
+template <int D, bool GENERAL>
+__device__ __forceinline__ TileRef tile_at(const AttnParams& p, const Smem<D>& sm, int i) {
+  TileRef t = tile_ref(p, sm.desc[i]);
+  t.kbits = 0;
+  if (GENERAL) {
+    const uint64_t b = sm.kbits[i];
+    // readfirstlane returns int: widen through uint32_t (no sign extension)
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    t.kbits = (uint64_t)lo | ((uint64_t)hi << 32);
+  }
   return t;
 }
 
@@ -626,13 +645,11 @@ __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t
 #pragma unroll
       for (int j = 0; j < 8; ++j) a[j] = (__bf16)0.0f;
       if (GENERAL) {
-        const int kb = t.kb_start + (t.key0 + min(key, t.n_valid - 1)) / p.block_k;
+        // this key's k-block inside the tile, and the keep bits of its q-blocks
+        const int jk = ((t.key0 + key) >> p.block_k_log2) - (t.key0 >> p.block_k_log2);
+        const uint32_t qkeep = kvalid ? (uint32_t)(t.kbits >> (16 * jk)) >> (8 * hh) : 0u;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int slot = 8 * hh + j;
-          const bool keep = kvalid && slot < n_qbt && p.mask[(int64_t)(qb_lo + slot) * p.n_kb + kb] != 0;
-          a[j] = keep ? (__bf16)0.0f : (__bf16)MASK_BIAS;
-        }
+        for (int j = 0; j < 8; ++j) a[j] = ((qkeep >> j) & 1u) ? (__bf16)0.0f : (__bf16)MASK_BIAS;
       } else if (hh == 0) {
         a[0] = kvalid ? (__bf16)0.0f : (__bf16)MASK_BIAS;
       }
@@ -640,9 +657,7 @@ __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t
     }
     if (GENERAL) {
       // does any kept key of this tile reach this lane's query row?
-      const int kb_lo = t.kb_start + t.key0 / p.block_k;
-      const int kb_hi = t.kb_start + (t.key0 + t.n_valid - 1) / p.block_k;
-      for (int kb = kb_lo; kb <= kb_hi; ++kb) ws.seen |= p.mask[(int64_t)my_qb * p.n_kb + kb] != 0;
+      ws.seen |= (t.kbits & (0x0001000100010001ull << (my_qb - qb_lo))) != 0;
     }
   }
 
@@ -893,21 +908,31 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     // with the set of waves that have a kept (q-block, k-block) pair in each
     const int ncand = min(LIST_CAP, c_hi - cbase);
     uint32_t wmk[2];
+    uint64_t kbt[2];
     TileInfo ti[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = 2 * tid + i;
       wmk[i] = 0;
+      kbt[i] = 0;
       if (c < ncand) {
         const TileInfo t = tile_info(p, cbase + c);
         ti[i] = t;
         const AttnSegment& sg = p.seg[t.seg];
-        const int kb_lo = sg.kb_start + t.key0 / p.block_k;
-        const int kb_hi = sg.kb_start + (t.key0 + t.n_valid - 1) / p.block_k;
+        const int kb_lo = sg.kb_start + (t.key0 >> p.block_k_log2);
+        const int kb_hi = sg.kb_start + ((t.key0 + t.n_valid - 1) >> p.block_k_log2);
         uint32_t qbits = 0;
         for (int qb = qb_lo; qb <= qb_hi; ++qb) {
           bool any = false;
-          for (int kb = kb_lo; kb <= kb_hi && !any; ++kb) any = p.mask[(int64_t)qb * p.n_kb + kb] != 0;
+          if (GENERAL) {
+            for (int kb = kb_lo; kb <= kb_hi; ++kb)
+              if (p.mask[(int64_t)qb * p.n_kb + kb] != 0) {
+                any = true;
+                kbt[i] |= 1ull << (16 * (kb - kb_lo) + (qb - qb_lo));
+              }
+          } else {
+            for (int kb = kb_lo; kb <= kb_hi && !any; ++kb) any = p.mask[(int64_t)qb * p.n_kb + kb] != 0;
+          }
           if (any) qbits |= 1u << (qb - qb_lo);
         }
 #pragma unroll
@@ -928,8 +953,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     }
     {
       int pos = base + __popcll(b0 & lt) + __popcll(b1 & lt);
-      if (wmk[0]) sm.desc[pos++] = pack_desc(ti[0], wmk[0]);
-      if (wmk[1]) sm.desc[pos] = pack_desc(ti[1], wmk[1]);
+      if (wmk[0]) {
+        if (GENERAL) sm.kbits[pos] = kbt[0];
+        sm.desc[pos++] = pack_desc(ti[0], wmk[0]);
+      }
+      if (wmk[1]) {
+        if (GENERAL) sm.kbits[pos] = kbt[1];
+        sm.desc[pos] = pack_desc(ti[1], wmk[1]);
+      }
     }
     __syncthreads();
     if (total == 0) continue;
@@ -940,7 +971,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       // handling of the direct-to-LDS loads)
 #pragma unroll 1
       for (int it = 0; it < total; ++it) {
-        const TileRef t = tile_ref(p, sm.desc[it]);
+        const TileRef t = tile_at<D, GENERAL>(p, sm, it);
         const bool direct_k = SCALED ? (k_wave && !t.is_int8) : stager;
         if (direct_k) issue_kdma<D, ST>(p, t, head, sm, it & 1, plan);
         if (stager) issue_stage<D, ST, SCALED>(p, t, head, st, plan);
@@ -967,7 +998,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       // and stored at the end of the step. Waves 4..7 run half a tile behind:
       // they multiply the previous tile's P with V first, then compute the
       // current tile's scores and softmax.
-      TileRef tn = tile_ref(p, sm.desc[0]);
+      TileRef tn = tile_at<D, GENERAL>(p, sm, 0);
       if (stager) {
         issue_kdma<D, ST>(p, tn, head, sm, 0, plan);
         issue_stage<D, ST, SCALED>(p, tn, head, st, plan);
@@ -984,7 +1015,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         const bool has_next = it + 1 < total;
         const int knext = kbuf ^ 1;
         const int vnext = (vbuf + 1 == NVBUF) ? 0 : vbuf + 1;
-        if (has_next) tn = tile_ref(p, sm.desc[it + 1]);
+        if (has_next) tn = tile_at<D, GENERAL>(p, sm, it + 1);
         // exact form: tile it's V exponent from its largest magnitude; the
         // stagers, whose registers still hold its bf16 V, store it again
         // times 2^e when e is not 0
@@ -1028,7 +1059,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     } else {
       // ---- scaled kernels. Prologue: first kept tile into K buffer 0 / V
       // buffer 0, the second one's staged loads into registers.
-      TileRef tc = tile_ref(p, sm.desc[0]);
+      TileRef tc = tile_at<D, GENERAL>(p, sm, 0);
       if (k_wave && !tc.is_int8) issue_kdma<D, ST>(p, tc, head, sm, 0, plan);
       issue_stage<D, ST, SCALED>(p, tc, head, st, plan);
       int e_cur = 0;
@@ -1036,7 +1067,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       commit_tile<D, ST, SCALED>(p, tc, st, sm, 0, 0, e_cur, i8_min_scale);
       TileRef tn1 = tc;
       if (total > 1) {
-        tn1 = tile_ref(p, sm.desc[1]);
+        tn1 = tile_at<D, GENERAL>(p, sm, 1);
         issue_stage<D, ST, SCALED>(p, tn1, head, st, plan);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1063,7 +1094,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         const int knext = kbuf ^ 1;
         const int vnext = (vbuf + 1 == NVBUF) ? 0 : vbuf + 1;
         TileRef tn2 = tn1;
-        if (has2) tn2 = tile_ref(p, sm.desc[it + 2]);
+        if (has2) tn2 = tile_at<D, GENERAL>(p, sm, it + 2);
         int e_next = 0;
         if constexpr (EXACT) {
           if (has1) e_next = exact_v_exponent(sm, staged_magnitude<D, ST, SCALED>(tn1, st), tn1.is_int8, wave, lane);

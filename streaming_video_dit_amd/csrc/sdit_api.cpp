@@ -278,6 +278,7 @@ int fill_attn_params(const void* q, int32_t n_q, const sdit_kv_segment* segs, in
     P->n_qb = n_qb;
     P->block_q = block_q;
     P->block_k = block_k;
+    P->block_k_log2 = __builtin_ctz((unsigned)block_k);
     P->grid = n_qt * n_heads;   // one workgroup per unit; a balanced launch re-plans it
     P->cu_per_xcd = 1;
     const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / sqrt((double)head_dim);

@@ -92,6 +92,7 @@ struct AttnParams {
   int32_t n_qb;        // mask rows
   int32_t block_q;
   int32_t block_k;
+  int32_t block_k_log2;
   float scale_log2;    // softmax_scale * log2(e)
   // Balanced launch. The work units (head, query tile) are dealt to the XCDs
   // in contiguous ranges; on an XCD with R units past its last full wave of

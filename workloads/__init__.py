@@ -160,6 +160,12 @@ WORKLOADS: Dict[str, Config] = {
     "bsa_sr": Config("bsa_sr", 12, 128, 8, 66, 66, 0, [34848], [False], 128,
                      "bsa", 4, rope=False, bsa_frame_tokens=66 * 66,
                      description="block-sparse video SR self-attention"),
+    # The same clip and mask rule at 32-token blocks (a fine mask: 64-key
+    # tiles hold two k-blocks, 256-row workgroups eight q-blocks), for timing
+    # the per-q-block masking path.
+    "bsa_sr_b32": Config("bsa_sr_b32", 12, 128, 8, 66, 66, 0, [34848], [False], 32,
+                         "bsa", 9, rope=False, bsa_frame_tokens=66 * 66,
+                         description="block-sparse video SR self-attention, 32-token blocks"),
     # Staggered chunks in one forward (Wave Forcing summary: block-causal
     # attention, later chunks read earlier ones): four Wan-1.3B chunks of
     # 3 x 30 x 52 tokens attend to the text cache, three history chunks and
