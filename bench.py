@@ -4,7 +4,10 @@
 One step = one layer-chunk of the hot path on seeded synthetic inputs already
 resident in HBM:
     qknorm_rope3d(chunk q, k)            (skipped by the self-attention SR workload)
-    kv_quant_int8(chunk K), (chunk V)    (int8-cache workload: the steady-state cache write)
+    kv_quant_int8(chunk K), (chunk V)    (int8-cache workload: the steady-state cache write;
+                                          fused with the line above into one
+                                          qknorm_rope3d_kv_quant_int8 pass unless
+                                          --unfused-cache-write)
     attn_fwd_balanced(q, [cache segments..., current chunk])
 
 The attention call is sdit_attn_fwd_balanced with the library's own plan:
@@ -77,7 +80,7 @@ class Step:
     """Device buffers and the launch sequence of one layer-chunk."""
 
     def __init__(self, cfg: W.Config, torch, sdit, kv_parts: int = 1, launch: str = "balanced",
-                 split_tile: int = -1):
+                 split_tile: int = -1, fused_cache_write: bool = True):
         self.cfg, self.torch, self.sdit = cfg, torch, sdit
         inp = W.make_inputs(cfg)
         self.inp = inp
@@ -142,6 +145,7 @@ class Step:
             self.split_tile = split_tile
             self.plan = sdit.attn_balanced_plan(n, H, self.n_tiles, cus, split_tile)
         self.quant_chunk = any(cfg.seg_int8)
+        self.fused = fused_cache_write and self.quant_chunk and cfg.rope and cfg.n_chunks == 1
         if self.quant_chunk:
             self.ck = torch.empty((n, H, d), dtype=torch.int8, device="cuda")
             self.cv = torch.empty((n, H, d), dtype=torch.int8, device="cuda")
@@ -153,15 +157,22 @@ class Step:
     def run(self, ev_before=None, ev_after=None, ev_merge=None):
         cfg, sdit = self.cfg, self.sdit
         H, d, n = cfg.n_heads, cfg.head_dim, cfg.n_q
-        if cfg.rope:
+        if self.fused:
+            # rotated q, k and the chunk's int8 cache entries in one pass
             dt, dh, dw = cfg.split
-            for c in range(cfg.n_chunks):
-                r = W.chunk_rows(cfg, c)
-                sdit.qknorm_rope3d(self.q_in[r], self.k_in[r], self.q[r], self.k[r], self.gq, self.gk, cfg.T,
-                                   cfg.Hl, cfg.Wl, cfg.t0 + c * cfg.T, H, d, dt, dh, dw, cfg.theta, cfg.eps)
-        if self.quant_chunk:   # single-chunk workloads only
-            sdit.kv_quant_int8(self.k, self.ck, self.sk, n, H, d)
-            sdit.kv_quant_int8(self.v, self.cv, self.sv, n, H, d)
+            sdit.qknorm_rope3d_kv_quant_int8(self.q_in, self.k_in, self.v, self.q, self.k, self.ck, self.sk, self.cv,
+                                             self.sv, self.gq, self.gk, cfg.T, cfg.Hl, cfg.Wl, cfg.t0, H, d, dt, dh,
+                                             dw, cfg.theta, cfg.eps)
+        else:
+            if cfg.rope:
+                dt, dh, dw = cfg.split
+                for c in range(cfg.n_chunks):
+                    r = W.chunk_rows(cfg, c)
+                    sdit.qknorm_rope3d(self.q_in[r], self.k_in[r], self.q[r], self.k[r], self.gq, self.gk, cfg.T,
+                                       cfg.Hl, cfg.Wl, cfg.t0 + c * cfg.T, H, d, dt, dh, dw, cfg.theta, cfg.eps)
+            if self.quant_chunk:   # single-chunk workloads only
+                sdit.kv_quant_int8(self.k, self.ck, self.sk, n, H, d)
+                sdit.kv_quant_int8(self.v, self.cv, self.sv, n, H, d)
         if cfg.window:
             for src, dst in ((self.q_in, self.q_w), (self.k_in, self.k_w), (self.v, self.v_w)):
                 sdit.window_permute(src, dst, cfg.T, cfg.Hl, cfg.Wl, H, d, cfg.window)
@@ -314,8 +325,28 @@ def measure_hbm_kernels(cfg: W.Config, torch, sdit, steps: int, warmup: int):
         t = _time_rotating(torch, lambda i: sdit.qknorm_rope3d(qs[i], ks[i], qo[i], ko[i], gq, gk, cfg.T, cfg.Hl, cfg.Wl,
                                                                cfg.t0, H, d, dt, dh, dw, cfg.theta, cfg.eps),
                            ns, steps, warmup)
-        res["qknorm_rope3d_chunk"] = _hbm_entry(f"qknorm_rope3d_kernel<{d}>", (m, H, d), nbytes, ns, t)
+        res["qknorm_rope3d_chunk"] = _hbm_entry(f"qknorm_rope3d_kernel<{d}, false>", (m, H, d), nbytes, ns, t)
         del qs, ks, qo, ko
+        if any(cfg.seg_int8):
+            # the fused pass: q, k, v read, q and k written, int8 codes + fp32 scales of k and v written
+            v0 = inp.v[r]
+            nbytes = 3 * 2 * m * H * d + 2 * 2 * m * H * d + 2 * (m * H * d + 4 * m * H) + 2 * 4 * d
+            ns = sets_for(nbytes)
+            qs = [_dev(q0, torch) for _ in range(ns)]
+            ks = [_dev(k0, torch) for _ in range(ns)]
+            vs = [_dev(v0, torch) for _ in range(ns)]
+            qo = [torch.empty_like(qs[0]) for _ in range(ns)]
+            ko = [torch.empty_like(ks[0]) for _ in range(ns)]
+            kc = [torch.empty((m, H, d), dtype=torch.int8, device="cuda") for _ in range(ns)]
+            vc = [torch.empty((m, H, d), dtype=torch.int8, device="cuda") for _ in range(ns)]
+            ksc = [torch.empty((m, H), dtype=torch.float32, device="cuda") for _ in range(ns)]
+            vsc = [torch.empty((m, H), dtype=torch.float32, device="cuda") for _ in range(ns)]
+            t = _time_rotating(torch, lambda i: sdit.qknorm_rope3d_kv_quant_int8(
+                qs[i], ks[i], vs[i], qo[i], ko[i], kc[i], ksc[i], vc[i], vsc[i], gq, gk, cfg.T, cfg.Hl, cfg.Wl,
+                cfg.t0, H, d, dt, dh, dw, cfg.theta, cfg.eps), ns, steps, warmup)
+            res["qknorm_rope3d_kv_quant_int8_chunk"] = _hbm_entry(f"qknorm_rope3d_kernel<{d}, true>", (m, H, d),
+                                                                  nbytes, ns, t)
+            del qs, ks, vs, qo, ko, kc, vc, ksc, vsc
     n_cache = sum(cfg.seg_lens[:cfg.n_cached])
     for label, n_tok in (("kv_quant_int8_chunk", cfg.chunk_tokens), ("kv_quant_int8_cache", n_cache)):
         if n_tok == 0:
@@ -481,6 +512,8 @@ def main():
                     help="attention entry point: sdit_attn_fwd_balanced (library plan) or sdit_attn_fwd")
     ap.add_argument("--split-tile", type=int, default=-1,
                     help="balanced launch: key tile of the cut (-1: the library's plan, 0: none)")
+    ap.add_argument("--unfused-cache-write", action="store_true",
+                    help="int8-cache workload: qknorm_rope3d and two kv_quant_int8 launches instead of the fused pass")
     ap.add_argument("--with-hbm", action="store_true",
                     help="also time qknorm_rope3d and kv_quant_int8 alone (rotated input sets) against 8 TB/s")
     ap.add_argument("--with-norms", action="store_true",
@@ -518,7 +551,8 @@ def main():
 
     cfg = W.WORKLOADS[args.workload]
     clocks = {"before": read_clocks()}
-    step = Step(cfg, torch, sdit, args.kv_parts, args.launch, args.split_tile)
+    step = Step(cfg, torch, sdit, args.kv_parts, args.launch, args.split_tile,
+                fused_cache_write=not args.unfused_cache_write)
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -555,7 +589,8 @@ def main():
                    "kept_tiles": int(step.inp.mask.sum()), "mask_tiles": int(step.inp.mask.size),
                    "effective_gflop": round(step.flops / 1e9, 3), "parallelism": "none (1 GPU)",
                    "launch": args.launch if args.kv_parts == 1 else "split-kv",
-                   "key_tiles": step.n_tiles, "cut_at_tile": step.plan[0], "attn_workgroups": step.plan[1]},
+                   "key_tiles": step.n_tiles, "cut_at_tile": step.plan[0], "attn_workgroups": step.plan[1],
+                   "cache_write": "fused" if step.fused else ("separate" if step.quant_chunk else "none")},
         "attn_ms": round(attn_avg, 5),
         "attn_ms_median": round(float(np.median(attn_ms)), 5),
         "attn_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5), round(float(np.percentile(attn_ms, 90)), 5)],

@@ -110,6 +110,30 @@ int sdit_qknorm_rope3d(const void* q_in, const void* k_in, void* q_out, void* k_
                        int32_t d_t, int32_t d_h, int32_t d_w,
                        float theta, float eps, void* stream);
 
+/* sdit_qknorm_rope3d of the chunk's q and k, together with the int8 cache
+ * entries of the chunk (the per-(token, head) int8 K/V cache of the
+ * Joy-face_change_optimized README, section 1, int8 K/V bullet, written for
+ * later chunks while this one attends to its own bf16 k and v): one pass
+ * that reads q_in, k_in and v_in once and writes
+ *   q_out, k_out   as sdit_qknorm_rope3d (bit for bit),
+ *   k_codes/_scales  sdit_kv_quant_int8 of k_out (from the rounded bf16
+ *                  values, so the codes are exactly those of quantising
+ *                  k_out afterwards, without reading it back),
+ *   v_codes/_scales  sdit_kv_quant_int8 of v_in.
+ *   v_in           bf16 [T*Hl*Wl][n_heads][head_dim], 16-byte aligned
+ *   k_codes, v_codes  int8 [T*Hl*Wl][n_heads][head_dim], 16-byte aligned
+ *   k_scales, v_scales  fp32 [T*Hl*Wl][n_heads], 4-byte aligned
+ * Other arguments and rules as sdit_qknorm_rope3d; the codes and scales must
+ * not overlap each other or any other argument, nor q_out/k_out v_in. */
+int sdit_qknorm_rope3d_kv_quant_int8(const void* q_in, const void* k_in, const void* v_in,
+                                     void* q_out, void* k_out,
+                                     int8_t* k_codes, float* k_scales, int8_t* v_codes, float* v_scales,
+                                     const float* gamma_q, const float* gamma_k,
+                                     int32_t T, int32_t Hl, int32_t Wl, int32_t t0,
+                                     int32_t n_heads, int32_t head_dim,
+                                     int32_t d_t, int32_t d_h, int32_t d_w,
+                                     float theta, float eps, void* stream);
+
 /* Symmetric int8 quantisation of a K or V tensor, one fp32 scale per
  * (token, head) (Joy-face_change_optimized README, section 1, int8 K/V
  * bullet). Call once for K and once for V.
@@ -296,6 +320,13 @@ int sdit_validate_qknorm_rope3d_args(const void* q_in, const void* k_in, void* q
                                      int32_t n_heads, int32_t head_dim,
                                      int32_t d_t, int32_t d_h, int32_t d_w,
                                      float theta, float eps);
+int sdit_validate_qknorm_rope3d_kv_quant_int8_args(const void* q_in, const void* k_in, const void* v_in,
+                                                   void* q_out, void* k_out, const int8_t* k_codes,
+                                                   const float* k_scales, const int8_t* v_codes,
+                                                   const float* v_scales, const float* gamma_q,
+                                                   const float* gamma_k, int32_t T, int32_t Hl, int32_t Wl,
+                                                   int32_t t0, int32_t n_heads, int32_t head_dim,
+                                                   int32_t d_t, int32_t d_h, int32_t d_w, float theta, float eps);
 int sdit_validate_kv_quant_args(const void* x, const int8_t* codes, const float* scales,
                                 int32_t n_tok, int32_t n_heads, int32_t head_dim);
 int sdit_validate_attn_args(const void* q, int32_t n_q,

@@ -55,6 +55,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.sdit_last_error.restype = ctypes.c_char_p
     L.sdit_qknorm_rope3d.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp] + [_i32] * 9 + [_f32, _f32, _vp]
     L.sdit_validate_qknorm_rope3d_args.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp] + [_i32] * 9 + [_f32, _f32]
+    L.sdit_qknorm_rope3d_kv_quant_int8.argtypes = [_vp] * 11 + [_i32] * 9 + [_f32, _f32, _vp]
+    L.sdit_validate_qknorm_rope3d_kv_quant_int8_args.argtypes = [_vp] * 11 + [_i32] * 9 + [_f32, _f32]
     L.sdit_kv_quant_int8.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _vp]
     L.sdit_validate_kv_quant_args.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32]
     L.sdit_attn_fwd.argtypes = [_vp, _i32, ctypes.POINTER(KVSegment), _i32, _vp, _i32, _i32, _i32, _i32, _f32,
@@ -84,7 +86,8 @@ def load_library(path: str) -> ctypes.CDLL:
               "sdit_validate_kv_quant_args", "sdit_attn_fwd", "sdit_validate_attn_args",
               "sdit_attn_fwd_partial", "sdit_validate_attn_partial_args", "sdit_attn_merge",
               "sdit_validate_attn_merge_args", "sdit_attn_fwd_balanced", "sdit_validate_attn_balanced_args",
-              "sdit_attn_balanced_plan", "sdit_attn_fwd_balanced_static"):
+              "sdit_attn_balanced_plan", "sdit_attn_fwd_balanced_static", "sdit_qknorm_rope3d_kv_quant_int8",
+              "sdit_validate_qknorm_rope3d_kv_quant_int8_args"):
         getattr(L, n).restype = ctypes.c_int
     if L.sdit_abi_version() != ABI_VERSION:
         raise ImportError(f"{path} ABI {L.sdit_abi_version()} != binding ABI {ABI_VERSION}")
@@ -129,6 +132,24 @@ def qknorm_rope3d(q_in, k_in, q_out, k_out, gamma_q, gamma_k, T: int, Hl: int, W
     """sdit_qknorm_rope3d."""
     _check(lib().sdit_qknorm_rope3d(_ptr(q_in), _ptr(k_in), _ptr(q_out), _ptr(k_out), _ptr(gamma_q), _ptr(gamma_k),
                                    T, Hl, Wl, t0, n_heads, head_dim, d_t, d_h, d_w, theta, eps, _stream(stream)))
+
+
+def qknorm_rope3d_kv_quant_int8(q_in, k_in, v_in, q_out, k_out, k_codes, k_scales, v_codes, v_scales, gamma_q,
+                                gamma_k, T: int, Hl: int, Wl: int, t0: int, n_heads: int, head_dim: int, d_t: int,
+                                d_h: int, d_w: int, theta: float = 1.0e4, eps: float = 1.0e-6, stream=None) -> None:
+    """sdit_qknorm_rope3d_kv_quant_int8."""
+    _check(lib().sdit_qknorm_rope3d_kv_quant_int8(
+        _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(q_out), _ptr(k_out), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+        _ptr(v_scales), _ptr(gamma_q), _ptr(gamma_k), T, Hl, Wl, t0, n_heads, head_dim, d_t, d_h, d_w, theta, eps,
+        _stream(stream)))
+
+
+def validate_qknorm_rope3d_kv_quant_int8_args(q_in, k_in, v_in, q_out, k_out, k_codes, k_scales, v_codes, v_scales,
+                                              gamma_q, gamma_k, T, Hl, Wl, t0, n_heads, head_dim, d_t, d_h, d_w,
+                                              theta=1.0e4, eps=1.0e-6) -> int:
+    return lib().sdit_validate_qknorm_rope3d_kv_quant_int8_args(
+        _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(q_out), _ptr(k_out), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+        _ptr(v_scales), _ptr(gamma_q), _ptr(gamma_k), T, Hl, Wl, t0, n_heads, head_dim, d_t, d_h, d_w, theta, eps)
 
 
 def kv_quant_int8(x, codes, scales, n_tok: int, n_heads: int, head_dim: int, stream=None) -> None:

@@ -59,30 +59,8 @@ __global__ __launch_bounds__(kThreads) void kv_quant_int8_kernel(QuantParams p) 
       x[2 * i] = bf16_lo(w[i]);
       x[2 * i + 1] = bf16_hi(w[i]);
     }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-
-    const float scale = amax / 127.0f;
-    uint32_t packed[2] = {0u, 0u};
-    if (scale >= 0x1p-100f) {
-      const float y = (float)(1.0 / (double)scale);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float q0 = x[i] * y;
-        const float q = fmaf(fmaf(-q0, scale, x[i]), y, q0);
-        const float c = fminf(fmaxf(rintf(q), -127.f), 127.f);
-        packed[i / 4] |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * (i % 4));
-      }
-    } else if (amax > 0.f) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float c = fminf(fmaxf(rintf(x[i] / scale), -127.f), 127.f);
-        packed[i / 4] |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * (i % 4));
-      }
-    }
+    uint32_t packed[2];
+    const float scale = quant_row8<LPR>(x, packed);
     if (row < p.n_rows) {
       *reinterpret_cast<uint2*>(p.codes + row * D + lane_in_row * 8) = make_uint2(packed[0], packed[1]);
       if (lane_in_row == 0) p.scales[row] = scale;

@@ -12,24 +12,34 @@
 // that each own 8 consecutive columns (16 B per row, coalesced 256 B rows).
 // A lane's four rotation angles depend only on the token, so they are
 // computed once per unit and reused for the unit's 2 * kHeadsPerUnit rows,
-// whose loads are all issued before the angle math, together with the loads
-// of the group's next unit.
+// whose loads are all issued before the angle math.
 // The arithmetic is fp64 (full rate on CDNA4 vector units, so it costs the
 // same as fp32 here), ending in one correctly rounded fp64 -> bf16
 // conversion. In fp32 a rotation whose two products nearly cancel loses
 // several bf16 ulps of its small result; in fp64 every output is within one
 // ulp of the exact value.
+//
+// The fused form (sdit_qknorm_rope3d_kv_quant_int8) also writes the int8
+// cache entries of the chunk: each unit loads the v rows of its heads with
+// the q and k rows, and quantises the rotated k rows from their bf16 output
+// (still in registers, never read back) and the v rows as they are, with the
+// arithmetic of kv_quant_int8 (quant_row8), so the codes and scales are the
+// ones sdit_kv_quant_int8 of k_out and v would give.
 #include "sdit_internal.h"
 
 namespace sdit {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kHeadsPerUnit = 4;
-// Workgroups of a launch: 1024 x 16 units per sweep. Measured on MI355X with
-// rotated buffers: the Wan chunk (14040 units, one sweep) is as fast as one unit
-// per 16-lane group, the Large-DiT chunk (24960 units) 5% faster (40.4 -> 38.3 us);
-// 512 is the same, 256 much slower (34 and 53 us).
+// Two heads per unit, each unit's loads issued when the unit starts (not a
+// unit ahead): the registers then allow more rows in flight per CU. Measured
+// on MI355X with rotated buffers against four heads with the next unit's
+// loads issued a unit ahead: Wan chunk 26.8 -> 24.6 us, and the fused form
+// with the chunk's int8 cache entries 53.2 -> 33.6 us (the three separate
+// launches take 45.6 us).
+constexpr int kHeadsPerUnit = 2;
+// Workgroups of a launch: 1024 x 16 units per sweep (512 was as fast, 256
+// much slower; 2048 no faster).
 constexpr int kMaxBlocks = 1024;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -76,23 +86,28 @@ __device__ __forceinline__ void sincos_f64(double x, double& s, double& c) {
   c = ((q + 1) & 2) ? -c0 : c0;
 }
 
-// The loads of a unit's 2 * kHeadsPerUnit rows (q rows, then k rows).
-template <int D>
-__device__ __forceinline__ void load_unit(const RopeParams& p, int tok, int h0, int nh, int c0, uint4 (&raw)[2 * kHeadsPerUnit]) {
+// Rows per unit: q and k rows (and v rows in the fused form).
+template <bool QUANT>
+constexpr int unit_rows() { return (QUANT ? 3 : 2) * kHeadsPerUnit; }
+
+// The loads of a unit's rows (q rows, then k rows, then v rows).
+template <int D, bool QUANT>
+__device__ __forceinline__ void load_unit(const RopeParams& p, int tok, int h0, int nh, int c0,
+                                          uint4 (&raw)[unit_rows<QUANT>()]) {
 #pragma unroll
-  for (int i = 0; i < 2 * kHeadsPerUnit; ++i) {
+  for (int i = 0; i < unit_rows<QUANT>(); ++i) {
     const int hi = i % kHeadsPerUnit;
-    const uint16_t* in = i < kHeadsPerUnit ? p.q_in : p.k_in;
+    const uint16_t* in = i < kHeadsPerUnit ? p.q_in : (i < 2 * kHeadsPerUnit ? p.k_in : p.v_in);
     raw[i] = hi < nh ? *reinterpret_cast<const uint4*>(in + ((int64_t)tok * p.n_heads + h0 + hi) * D + c0)
                      : make_uint4(0, 0, 0, 0);
   }
 }
 
 // A 16-lane group walks units unit, unit + S, unit + 2S, ... (S units in the
-// grid) and issues the loads of its next unit before it computes and stores
-// the current one, so loads, arithmetic and stores of successive units overlap.
-template <int D>
+// grid).
+template <int D, bool QUANT>
 __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
+  constexpr int NR = unit_rows<QUANT>();
   constexpr int LPR = D / 8;
   constexpr int UNITS_PER_BLOCK = kThreads / LPR;
   const int lane_in_row = threadIdx.x % LPR;
@@ -115,15 +130,13 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
 
   int tok = (int)(unit / n_hg);
   int h0 = (int)(unit % n_hg) * kHeadsPerUnit;
-  uint4 raw[2 * kHeadsPerUnit];
-  load_unit<D>(p, tok, h0, min(kHeadsPerUnit, p.n_heads - h0), c0, raw);
+  uint4 raw[NR];
+  load_unit<D, QUANT>(p, tok, h0, min(kHeadsPerUnit, p.n_heads - h0), c0, raw);
   for (;;) {
     const int nh = min(kHeadsPerUnit, p.n_heads - h0);
     const int64_t next = unit + stride;
     const bool more = next < n_units;
     const int tok_n = (int)(next / n_hg), h0_n = (int)(next % n_hg) * kHeadsPerUnit;
-    uint4 nxt[2 * kHeadsPerUnit];
-    if (more) load_unit<D>(p, tok_n, h0_n, min(kHeadsPerUnit, p.n_heads - h0_n), c0, nxt);
 
     // Token position on the three axes.
     const int HW = p.Hl * p.Wl;
@@ -166,13 +179,47 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
         o[e] = f64x2_to_bf16x2(r0, r1);
       }
       uint16_t* out = t ? p.k_out : p.q_out;
-      if (hi < nh)
-        *reinterpret_cast<uint4*>(out + ((int64_t)tok * p.n_heads + h0 + hi) * D + c0) =
-            make_uint4(o[0], o[1], o[2], o[3]);
+      const int64_t row = (int64_t)tok * p.n_heads + h0 + hi;
+      if (hi < nh) *reinterpret_cast<uint4*>(out + row * D + c0) = make_uint4(o[0], o[1], o[2], o[3]);
+      if (QUANT && t == 1) {
+        // int8 cache entry of the rotated k row, from its bf16 output
+        float xq[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xq[2 * e] = bf16_lo(o[e]);
+          xq[2 * e + 1] = bf16_hi(o[e]);
+        }
+        uint32_t packed[2];
+        const float scale = quant_row8<LPR>(xq, packed);
+        if (hi < nh) {
+          *reinterpret_cast<uint2*>(p.k_codes + row * D + c0) = make_uint2(packed[0], packed[1]);
+          if (lane_in_row == 0) p.k_scales[row] = scale;
+        }
+      }
+    }
+    if (QUANT) {
+      // int8 cache entries of the v rows
+#pragma unroll
+      for (int hi = 0; hi < kHeadsPerUnit; ++hi) {
+        const uint4 w = raw[2 * kHeadsPerUnit + hi];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        float xv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[2 * e] = bf16_lo(ww[e]);
+          xv[2 * e + 1] = bf16_hi(ww[e]);
+        }
+        uint32_t packed[2];
+        const float scale = quant_row8<LPR>(xv, packed);
+        const int64_t row = (int64_t)tok * p.n_heads + h0 + hi;
+        if (hi < nh) {
+          *reinterpret_cast<uint2*>(p.v_codes + row * D + c0) = make_uint2(packed[0], packed[1]);
+          if (lane_in_row == 0) p.v_scales[row] = scale;
+        }
+      }
     }
     if (!more) break;
-#pragma unroll
-    for (int i = 0; i < 2 * kHeadsPerUnit; ++i) raw[i] = nxt[i];
+    load_unit<D, QUANT>(p, tok_n, h0_n, min(kHeadsPerUnit, p.n_heads - h0_n), c0, raw);
     unit = next;
     tok = tok_n;
     h0 = h0_n;
@@ -186,7 +233,10 @@ hipError_t launch(const RopeParams& p, hipStream_t stream) {
   const int64_t n_units = (int64_t)p.n_tok * n_hg;
   int64_t blocks = (n_units + UNITS_PER_BLOCK - 1) / UNITS_PER_BLOCK;
   blocks = min(blocks, (int64_t)kMaxBlocks);
-  hipLaunchKernelGGL(qknorm_rope3d_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  if (p.k_codes != nullptr)
+    hipLaunchKernelGGL((qknorm_rope3d_kernel<D, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((qknorm_rope3d_kernel<D, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -114,14 +114,14 @@ SDIT_API int sdit_validate_qknorm_rope3d_args(const void* q_in, const void* k_in
   return ok();
 }
 
-SDIT_API int sdit_qknorm_rope3d(const void* q_in, const void* k_in, void* q_out, void* k_out,
-                                const float* gamma_q, const float* gamma_k, int32_t T, int32_t Hl, int32_t Wl,
-                                int32_t t0, int32_t n_heads, int32_t head_dim, int32_t d_t, int32_t d_h,
-                                int32_t d_w, float theta, float eps, void* stream) {
-  int st = sdit_validate_qknorm_rope3d_args(q_in, k_in, q_out, k_out, gamma_q, gamma_k, T, Hl, Wl, t0, n_heads,
-                                            head_dim, d_t, d_h, d_w, theta, eps);
-  if (st != SDIT_OK) return st;
-  sdit::RopeParams p;
+namespace {
+
+// Kernel arguments of a validated qknorm_rope3d call (no int8 outputs).
+void fill_rope_params(sdit::RopeParams* P, const void* q_in, const void* k_in, void* q_out, void* k_out,
+                      const float* gamma_q, const float* gamma_k, int32_t T, int32_t Hl, int32_t Wl, int32_t t0,
+                      int32_t n_heads, int32_t d_t, int32_t d_h, int32_t d_w, float theta, float eps) {
+  sdit::RopeParams& p = *P;
+  memset(&p, 0, sizeof(p));
   p.q_in = (const uint16_t*)q_in;
   p.k_in = (const uint16_t*)k_in;
   p.q_out = (uint16_t*)q_out;
@@ -137,17 +137,85 @@ SDIT_API int sdit_qknorm_rope3d(const void* q_in, const void* k_in, void* q_out,
   p.d_h = d_h;
   p.d_w = d_w;
   // pair j of an axis of width d_a turns at theta^(-2j/d_a), in column order t | h | w
-  {
-    int c = 0;
-    for (int a = 0; a < 3; ++a) {
-      const int da = a == 0 ? d_t : (a == 1 ? d_h : d_w);
-      for (int j = 0; j < da / 2; ++j) p.omega[c++] = pow((double)theta, -2.0 * j / da);
-    }
-    for (; c < 64; ++c) p.omega[c] = 0.0;
+  int c = 0;
+  for (int a = 0; a < 3; ++a) {
+    const int da = a == 0 ? d_t : (a == 1 ? d_h : d_w);
+    for (int j = 0; j < da / 2; ++j) p.omega[c++] = pow((double)theta, -2.0 * j / da);
   }
+  for (; c < 64; ++c) p.omega[c] = 0.0;
   p.eps = eps;
+}
+
+}  // namespace
+
+SDIT_API int sdit_qknorm_rope3d(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                                const float* gamma_q, const float* gamma_k, int32_t T, int32_t Hl, int32_t Wl,
+                                int32_t t0, int32_t n_heads, int32_t head_dim, int32_t d_t, int32_t d_h,
+                                int32_t d_w, float theta, float eps, void* stream) {
+  int st = sdit_validate_qknorm_rope3d_args(q_in, k_in, q_out, k_out, gamma_q, gamma_k, T, Hl, Wl, t0, n_heads,
+                                            head_dim, d_t, d_h, d_w, theta, eps);
+  if (st != SDIT_OK) return st;
+  sdit::RopeParams p;
+  fill_rope_params(&p, q_in, k_in, q_out, k_out, gamma_q, gamma_k, T, Hl, Wl, t0, n_heads, d_t, d_h, d_w, theta, eps);
   if (p.n_tok == 0) return ok();
   return device_status(sdit::launch_qknorm_rope3d(p, head_dim, (hipStream_t)stream), "qknorm_rope3d");
+}
+
+SDIT_API int sdit_validate_qknorm_rope3d_kv_quant_int8_args(
+    const void* q_in, const void* k_in, const void* v_in, void* q_out, void* k_out, const int8_t* k_codes,
+    const float* k_scales, const int8_t* v_codes, const float* v_scales, const float* gamma_q,
+    const float* gamma_k, int32_t T, int32_t Hl, int32_t Wl, int32_t t0, int32_t n_heads, int32_t head_dim,
+    int32_t d_t, int32_t d_h, int32_t d_w, float theta, float eps) {
+  int st = sdit_validate_qknorm_rope3d_args(q_in, k_in, q_out, k_out, gamma_q, gamma_k, T, Hl, Wl, t0, n_heads,
+                                            head_dim, d_t, d_h, d_w, theta, eps);
+  if (st != SDIT_OK) return st;
+  const int64_t n_tok = (int64_t)T * Hl * Wl;
+  if (n_tok == 0) return ok();
+  if (v_in == nullptr || !aligned(v_in, 16))
+    return fail(SDIT_ERR_INVALID, "qknorm_rope3d_kv_quant_int8: v_in must be non-NULL and 16-byte aligned");
+  if (k_codes == nullptr || v_codes == nullptr || !aligned(k_codes, 16) || !aligned(v_codes, 16))
+    return fail(SDIT_ERR_INVALID, "qknorm_rope3d_kv_quant_int8: codes must be non-NULL and 16-byte aligned");
+  if (k_scales == nullptr || v_scales == nullptr || !aligned(k_scales, 4) || !aligned(v_scales, 4))
+    return fail(SDIT_ERR_INVALID, "qknorm_rope3d_kv_quant_int8: scales must be non-NULL and 4-byte aligned");
+  const int64_t rows = n_tok * n_heads, bytes = rows * head_dim * 2, cbytes = rows * head_dim, sbytes = rows * 4;
+  // every output apart from each other and from every input (q_out/k_out may
+  // equal q_in/k_in, already checked)
+  const void* outs[4] = {k_codes, k_scales, v_codes, v_scales};
+  const int64_t osz[4] = {cbytes, sbytes, cbytes, sbytes};
+  const void* others[8] = {q_in, k_in, v_in, q_out, k_out, gamma_q, gamma_k, nullptr};
+  const int64_t oth[8] = {bytes, bytes, bytes, bytes, bytes, head_dim * 4, head_dim * 4, 0};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlap(outs[i], osz[i], others[j], oth[j]))
+        return fail(SDIT_ERR_INVALID, "qknorm_rope3d_kv_quant_int8: codes/scales overlap another argument");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], osz[i], outs[j], osz[j]))
+        return fail(SDIT_ERR_INVALID, "qknorm_rope3d_kv_quant_int8: codes/scales overlap each other");
+  }
+  if (overlap(v_in, bytes, q_out, bytes) || overlap(v_in, bytes, k_out, bytes))
+    return fail(SDIT_ERR_INVALID, "qknorm_rope3d_kv_quant_int8: q_out/k_out overlap v_in");
+  return ok();
+}
+
+SDIT_API int sdit_qknorm_rope3d_kv_quant_int8(const void* q_in, const void* k_in, const void* v_in, void* q_out,
+                                              void* k_out, int8_t* k_codes, float* k_scales, int8_t* v_codes,
+                                              float* v_scales, const float* gamma_q, const float* gamma_k,
+                                              int32_t T, int32_t Hl, int32_t Wl, int32_t t0, int32_t n_heads,
+                                              int32_t head_dim, int32_t d_t, int32_t d_h, int32_t d_w, float theta,
+                                              float eps, void* stream) {
+  int st = sdit_validate_qknorm_rope3d_kv_quant_int8_args(q_in, k_in, v_in, q_out, k_out, k_codes, k_scales,
+                                                          v_codes, v_scales, gamma_q, gamma_k, T, Hl, Wl, t0,
+                                                          n_heads, head_dim, d_t, d_h, d_w, theta, eps);
+  if (st != SDIT_OK) return st;
+  sdit::RopeParams p;
+  fill_rope_params(&p, q_in, k_in, q_out, k_out, gamma_q, gamma_k, T, Hl, Wl, t0, n_heads, d_t, d_h, d_w, theta, eps);
+  p.v_in = (const uint16_t*)v_in;
+  p.k_codes = k_codes;
+  p.k_scales = k_scales;
+  p.v_codes = v_codes;
+  p.v_scales = v_scales;
+  if (p.n_tok == 0) return ok();
+  return device_status(sdit::launch_qknorm_rope3d(p, head_dim, (hipStream_t)stream), "qknorm_rope3d_kv_quant_int8");
 }
 
 // ------------------------------------------------------------------ kv_quant_int8

@@ -52,10 +52,52 @@ struct RopeParams {
   int32_t n_heads, d_t, d_h, d_w;
   double omega[64];    // rotation frequency of pair c/2: theta^(-2j/d_axis), computed on the host
   float eps;
+  // fused int8 cache write (sdit_qknorm_rope3d_kv_quant_int8), else NULL:
+  // codes and scales of the rotated k (from its bf16 output) and of v_in
+  const uint16_t* v_in;
+  int8_t* k_codes;
+  float* k_scales;
+  int8_t* v_codes;
+  float* v_scales;
 };
 hipError_t launch_qknorm_rope3d(const RopeParams& p, int head_dim, hipStream_t stream);
 
 // ---------------------------------------------------------------- kv_quant_int8
+// One row's share of the int8 quantisation (the kv_quant_int8 definition):
+// the calling lane holds 8 consecutive values x[] of a row spread over LPR
+// consecutive lanes (a power of two). Returns the row's scale (every lane)
+// and the lane's 8 codes packed in two words. The reciprocal is correctly
+// rounded (1/scale in fp64, rounded to binary32) and the quotient corrected
+// by Markstein's residual step, so q = RN(x / scale) exactly; rows with
+// scale < 2^-100 divide.
+template <int LPR>
+__device__ __forceinline__ float quant_row8(const float (&x)[8], uint32_t (&packed)[2]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float scale = amax / 127.0f;
+  packed[0] = packed[1] = 0u;
+  if (scale >= 0x1p-100f) {
+    const float y = (float)(1.0 / (double)scale);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q0 = x[i] * y;
+      const float q = fmaf(fmaf(-q0, scale, x[i]), y, q0);
+      const float c = fminf(fmaxf(rintf(q), -127.f), 127.f);
+      packed[i / 4] |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * (i % 4));
+    }
+  } else if (amax > 0.f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float c = fminf(fmaxf(rintf(x[i] / scale), -127.f), 127.f);
+      packed[i / 4] |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * (i % 4));
+    }
+  }
+  return scale;
+}
+
 struct QuantParams {
   const uint16_t* x;
   int8_t* codes;

@@ -61,6 +61,27 @@ def test_qknorm_validation():
     assert "axis split" in (v(d_t=40), sdit.last_error())[1]
 
 
+def test_qknorm_quant_validation():
+    def v(**kw):
+        a = _rope_args()
+        a.update(v_in=A16 + 80 * MB, k_codes=A16 + 96 * MB, k_scales=A16 + 104 * MB, v_codes=A16 + 112 * MB,
+                 v_scales=A16 + 120 * MB)
+        a.update(kw)
+        return sdit.validate_qknorm_rope3d_kv_quant_int8_args(**a)
+    assert v() == sdit.SDIT_OK
+    assert v(q_out=A16, k_out=A16 + 16 * MB) == sdit.SDIT_OK              # exact in place
+    assert v(d_t=40) == sdit.SDIT_ERR_INVALID                              # the plain call's checks come first
+    assert v(v_in=None) == sdit.SDIT_ERR_INVALID
+    assert v(k_codes=A16 + 96 * MB + 8) == sdit.SDIT_ERR_INVALID          # misaligned codes
+    assert v(v_scales=A16 + 120 * MB + 2) == sdit.SDIT_ERR_INVALID        # misaligned scales
+    assert v(k_scales=A16 + 96 * MB + 4096) == sdit.SDIT_ERR_INVALID      # scales inside the k codes
+    assert v(v_codes=A16 + 80 * MB) == sdit.SDIT_ERR_INVALID              # codes over v_in
+    assert v(k_codes=A16 + 64 * MB) == sdit.SDIT_ERR_INVALID              # codes over gamma
+    assert v(v_in=A16 + 32 * MB) == sdit.SDIT_ERR_INVALID                 # q_out over v_in
+    assert v(T=0, q_in=None, v_in=None, k_codes=None) == sdit.SDIT_OK     # empty grid: no-op
+    assert v(head_dim=96, d_t=32, d_h=32, d_w=32) == sdit.SDIT_ERR_UNSUPPORTED
+
+
 def test_kv_quant_validation():
     v = sdit.validate_kv_quant_args
     assert v(A16, A16 + 16 * MB, A16 + 32 * MB, 100, 12, 128) == sdit.SDIT_OK

@@ -154,6 +154,59 @@ def test_qknorm_rope3d_other_splits(split, d):
     _check_rope(b, k, gk, geo)
 
 
+# ------------------------------------------------------------------ qknorm_rope3d + int8 cache entries, fused
+
+def _gpu_rope_quant(geo, q_bits, k_bits, v_bits, gq, gk, in_place=False):
+    import torch
+    import streaming_video_dit_amd as sdit
+    T, Hl, Wl, t0, (dt, dh, dw) = geo
+    n, H, d = q_bits.shape
+    qi, ki, vi = dev(q_bits), dev(k_bits), dev(v_bits)
+    qo, ko = (qi, ki) if in_place else (empty_bf16((n, H, d)), empty_bf16((n, H, d)))
+    kc = torch.full((n, H, d), 99, dtype=torch.int8, device="cuda")
+    vc = torch.full((n, H, d), 99, dtype=torch.int8, device="cuda")
+    ks = torch.full((n, H), float("nan"), dtype=torch.float32, device="cuda")
+    vs = torch.full((n, H), float("nan"), dtype=torch.float32, device="cuda")
+    sdit.qknorm_rope3d_kv_quant_int8(qi, ki, vi, qo, ko, kc, ks, vc, vs, dev(gq), dev(gk), T, Hl, Wl, t0, H, d,
+                                     dt, dh, dw, 1.0e4, 1.0e-6)
+    torch.cuda.synchronize()
+    return host_u16(qo), host_u16(ko), kc.cpu().numpy(), ks.cpu().numpy(), vc.cpu().numpy(), vs.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["tiny", "wan13b_int8", "five_heads_d128", "three_heads_d64_in_place"])
+def test_qknorm_rope3d_with_int8_cache_entries(case):
+    """One pass writing the rotated q, k and the int8 cache entries of k and
+    v: q/k bit for bit as sdit_qknorm_rope3d (within one ulp of the oracle),
+    codes and scales bit for bit as the oracle's quantisation of that k and of
+    v (head groups of 4 with a ragged last group: 5 and 3 heads)."""
+    if case in ("tiny", "wan13b_int8"):
+        cfg = W.WORKLOADS[case]
+        inp = W.make_inputs(cfg)
+        r = W.chunk_rows(cfg, 0)
+        q, k, v, gq, gk = inp.q[r], inp.k[r], inp.v[r], inp.gamma_q, inp.gamma_k
+        geo = (cfg.T, cfg.Hl, cfg.Wl, cfg.t0, cfg.split)
+    else:
+        H, d = (5, 128) if case == "five_heads_d128" else (3, 64)
+        geo = (3, 5, 7, 4, W.rope_split(d))
+        n = 3 * 5 * 7
+        q = W.normal_bf16(61, 0, (n, H, d))
+        k = W.normal_bf16(61, 1, (n, H, d), outlier_p=0.02, outlier_tid=5)
+        v = W.normal_bf16(61, 2, (n, H, d), outlier_p=0.02, outlier_tid=6)
+        v[0, 0, :] = 0                      # an all-zero v row
+        gq = W.uniform_f32(61, 3, (d,), 0.5, 1.5)
+        gk = W.uniform_f32(61, 4, (d,), 0.5, 1.5)
+    _say("qknorm_rope3d + int8 cache entries", case, q.shape)
+    qo, ko, kc, ks, vc, vs = _gpu_rope_quant(geo, q, k, v, gq, gk, in_place=case.endswith("in_place"))
+    pq, pk = _gpu_rope(geo, q, k, gq, gk)
+    assert np.array_equal(qo, pq) and np.array_equal(ko, pk), "q/k differ from sdit_qknorm_rope3d"
+    _check_rope(qo, q, gq, geo)
+    _check_rope(ko, k, gk, geo)
+    rkc, rks = oracle.kv_quant_int8(ko)
+    rvc, rvs = oracle.kv_quant_int8(v)
+    assert np.array_equal(ks.view(np.uint32), rks.view(np.uint32)) and np.array_equal(kc, rkc), "k codes/scales"
+    assert np.array_equal(vs.view(np.uint32), rvs.view(np.uint32)) and np.array_equal(vc, rvc), "v codes/scales"
+
+
 # ------------------------------------------------------------------ attention: tiny workload end to end
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_dense"])
