@@ -174,8 +174,13 @@ int sdit_kv_quant_int8(const void* x, int8_t* codes, float* scales,
  *   s_j = scale * q_i . k_j,  o_i = sum_j softmax(s)_j v_j,  lse_i = log sum_j e^{s_j};
  * a query with no visible key gets o_i = 0 and lse_i = -inf.
  * Scores accumulate in fp32 from bf16 q.k products; the probability-weighted
- * sum of V runs in fp16 with fp32 accumulation, so bf16 V values must stay
- * below 65504 in magnitude (int8 codes always fit).
+ * sum of V multiplies fp16 probabilities with V staged in fp16, accumulating
+ * in fp32. Any finite V is accepted: where fp16 would not hold a 64-key tile
+ * of V (bf16 values below 2^-17 or at 65536 and above, int8 row scales below
+ * 2^-14), the tile is staged times a power of two chosen from its largest
+ * magnitude and the accumulators are rescaled exactly (a workgroup whose
+ * result shows such data runs again in that form). int8 K row scales below
+ * about 1e-11 are out of contract (the score multiplier is floored).
  * Output must not overlap any input. */
 int sdit_attn_fwd(const void* q, int32_t n_q,
                   const sdit_kv_segment* segs, int32_t n_segs,
