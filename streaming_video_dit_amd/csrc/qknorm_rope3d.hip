@@ -165,8 +165,7 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope3d_kernel(RopeParams p) {
       double ss = 0.0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = fma(x[e], x[e], ss);
-#pragma unroll
-      for (int off = LPR / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+      ss = group_sum<LPR>(ss);
       const double inv = 1.0 / sqrt(ss / (double)D + (double)p.eps);
 
       uint32_t o[4];

@@ -70,13 +70,46 @@ hipError_t launch_qknorm_rope3d(const RopeParams& p, int head_dim, hipStream_t s
 // rounded (1/scale in fp64, rounded to binary32) and the quotient corrected
 // by Markstein's residual step, so q = RN(x / scale) exactly; rows with
 // scale < 2^-100 divide.
+// Reductions over a group of LPR (8 or 16) lanes aligned to a 16-lane DPP
+// row, in DPP moves (no LDS): swap neighbours, swap pairs inside the quad,
+// mirror the half-row, mirror the row. Each step combines disjoint lane sets
+// with a commutative op, so every lane of the group ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const long long u = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned int)hi << 32) | (unsigned int)lo));
+}
+template <int LPR>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(LPR == 8 || LPR == 16, "lane group of 8 or 16");
+  x = fmaxf(x, dpp_f32<0xB1>(x));
+  x = fmaxf(x, dpp_f32<0x4E>(x));
+  x = fmaxf(x, dpp_f32<0x141>(x));
+  if (LPR == 16) x = fmaxf(x, dpp_f32<0x140>(x));
+  return x;
+}
+template <int LPR>
+__device__ __forceinline__ double group_sum(double x) {
+  static_assert(LPR == 8 || LPR == 16, "lane group of 8 or 16");
+  x += dpp_f64<0xB1>(x);
+  x += dpp_f64<0x4E>(x);
+  x += dpp_f64<0x141>(x);
+  if (LPR == 16) x += dpp_f64<0x140>(x);
+  return x;
+}
+
 template <int LPR>
 __device__ __forceinline__ float quant_row8(const float (&x)[8], uint32_t (&packed)[2]) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  amax = group_max<LPR>(amax);
   const float scale = amax / 127.0f;
   packed[0] = packed[1] = 0u;
   if (scale >= 0x1p-100f) {
