@@ -166,7 +166,10 @@ int sdit_kv_quant_int8(const void* x, int8_t* codes, float* scales,
  *                partial.
  *   block_q, block_k   16, 32, 64 or 128
  *   head_dim     64 or 128
- *   softmax_scale  <= 0 selects 1/sqrt(head_dim)
+ *   softmax_scale  <= 0 selects 1/sqrt(head_dim); a positive scale below
+ *                2^-40 is rejected (SDIT_ERR_INVALID): masking adds a -1e30
+ *                bias to a key's raw score, which has to stay far below every
+ *                visible score once scaled
  *   out          bf16 [n_q][n_heads][head_dim]
  *   lse          fp32 [n_heads][n_q] natural-log sum of exponentials of the
  *                scaled scores, or NULL

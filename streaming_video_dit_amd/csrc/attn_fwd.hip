@@ -557,6 +557,16 @@ __device__ __forceinline__ void commit_tile(const AttnParams& p, const TileRef& 
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
+// x[n] *= (a of lane n of the caller's 16-lane row), n = N..15: a DPP row
+// broadcast folded into each multiply (v_mul_f32_dpp row_newbcast:n).
+template <int N>
+__device__ __forceinline__ void scale_by_row_lanes(f32x16& x, float a) {
+  if constexpr (N < 16) {
+    x[N] *= __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x150 + N, 0xF, 0xF, true));
+    scale_by_row_lanes<N + 1>(x, a);
+  }
+}
+
 __device__ __forceinline__ float swap_halves_max(float x) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
@@ -607,6 +617,21 @@ __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t
   constexpr int NDT = D / 32;
   // LDS operand reads in flight ahead of their MFMA (the scaled path needs the registers)
   constexpr int PF = SCALED ? 2 : 4;
+
+  // int8 tiles of the scaled kernels: per-key multipliers applied to the raw
+  // scores; every other tile: raw scores, scale_log2 folded into the
+  // exponent's FMA. Every lane of a 16-lane row needs the same 16 multipliers
+  // per subtile (its row lies in one lane half): lane n of the row reads the
+  // one for element n (key kt*32 + 8(n/4) + 4hh + n%4) here, ahead of the
+  // score MFMAs, and each multiply takes it by a DPP row broadcast; two
+  // 4-byte LDS reads per lane instead of eight 16-byte ones.
+  const bool per_key = SCALED && t.is_int8;
+  float kmul[2] = {1.f, 1.f};
+  if (SCALED) {
+    const int n16 = r & 15;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) kmul[kt] = ksc[kt * 32 + 8 * (n16 >> 2) + 4 * hh + (n16 & 3)];
+  }
 
   // ---- S^T = K Q^T for two 32-key subtiles; operand reads PF steps ahead,
   // scheduling fences keep the compiler from hoisting all of them
@@ -663,24 +688,15 @@ __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t
 
   // ---- scores in log2 units and the tile's row max
   float mt = -INFINITY;
-  if (SCALED) {
+  if (per_key) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 sc = *reinterpret_cast<const float4*>(&ksc[kt * 32 + 8 * g + 4 * hh]);
-        s[kt][4 * g + 0] *= sc.x;
-        s[kt][4 * g + 1] *= sc.y;
-        s[kt][4 * g + 2] *= sc.z;
-        s[kt][4 * g + 3] *= sc.w;
-      }
+    for (int kt = 0; kt < 2; ++kt) scale_by_row_lanes<0>(s[kt], kmul[kt]);
   }
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int e2 = 0; e2 < 16; e2 += 2) mt = max3(mt, s[kt][e2], s[kt][e2 + 1]);
-  // unscaled path: raw scores, scale_log2 folded into the exponent's FMA
-  const float cs = SCALED ? 1.0f : p.scale_log2;
+  const float cs = per_key ? 1.0f : p.scale_log2;
   mt = swap_halves_max(mt) * cs;
   if (mt < MASKED_MAX) mt = -INFINITY;   // nothing visible for this row in the tile
 

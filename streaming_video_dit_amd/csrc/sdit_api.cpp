@@ -274,6 +274,10 @@ int fill_attn_params(const void* q, int32_t n_q, const sdit_kv_segment* segs, in
     return fail(SDIT_ERR_INVALID, "attn_fwd: n_segs %d not in [1, %d]", n_segs, SDIT_MAX_SEGMENTS);
   if (segs == nullptr) return fail(SDIT_ERR_INVALID, "attn_fwd: segs is NULL");
   if (!isfinite(softmax_scale)) return fail(SDIT_ERR_INVALID, "attn_fwd: softmax_scale not finite");
+  // a masked key's -1e30 bias times the scale has to stay far below every
+  // visible score (the kernel takes maxima under -1e15 as "nothing visible")
+  if (softmax_scale > 0.f && softmax_scale < 0x1p-40f)
+    return fail(SDIT_ERR_INVALID, "attn_fwd: softmax_scale %g below 2^-40", (double)softmax_scale);
   if ((int64_t)n_q * n_heads > kMaxElems / head_dim) return fail(SDIT_ERR_INVALID, "attn_fwd: q too large");
   int64_t tiles = 0, kbs = 0;
   for (int s = 0; s < n_segs; ++s) {

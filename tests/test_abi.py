@@ -131,6 +131,9 @@ def test_attn_validation():
     assert v(n_q=-1) == sdit.SDIT_ERR_INVALID
     assert v(n_heads=0) == sdit.SDIT_ERR_INVALID
     assert v(softmax_scale=float("nan")) == sdit.SDIT_ERR_INVALID
+    assert v(softmax_scale=2.0 ** -41) == sdit.SDIT_ERR_INVALID    # the -1e30 mask bias would surface
+    assert v(softmax_scale=2.0 ** -40) == sdit.SDIT_OK
+    assert v(softmax_scale=-1.0) == sdit.SDIT_OK                   # selects 1/sqrt(head_dim)
     assert "segment 1" in (v(segs=_segs(s1=dict(dtype=sdit.SDIT_INT8))), sdit.last_error())[1]
 
 

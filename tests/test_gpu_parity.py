@@ -389,6 +389,17 @@ def test_attention_custom_softmax_scale():
     assert_attn_close(out, lse, O, LSE, "scale 0.03")
 
 
+@pytest.mark.parametrize("dtypes", [["bf16", "bf16"], ["int8", "bf16"]])
+def test_smallest_softmax_scale_keeps_masked_keys_out(dtypes):
+    """At the smallest accepted scale (2^-40) every visible score is ~0, so each
+    row averages V over its visible keys; a masked key's -1e30 bias, scaled,
+    must still rank as invisible (fine 16-token blocks, int8 and bf16 tiles)."""
+    q, segs, mask = _rand_case(23, 160, 2, 128, [96, 160], dtypes, 16, 16, 0.5, (3,))
+    out, lse = run_attn(q, segs, mask, 16, 16, softmax_scale=2.0 ** -40)
+    O, LSE = oracle.attention(q, segs, mask, 16, 16, softmax_scale=2.0 ** -40)
+    assert_attn_close(out, lse, O, LSE, "scale 2^-40")
+
+
 def test_attention_all_segments_empty_gives_zero_and_minus_inf():
     q = W.normal_bf16(1, 0, (40, 2, 64))
     segs = [{"k": np.zeros((0, 2, 64), np.uint16), "v": np.zeros((0, 2, 64), np.uint16), "dtype": "bf16"}]
