@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kThreads, QUANT ? 1 : 3) void qknorm_rope3d_kernel(
       // 1/sqrt(mean + eps): the hardware estimate (relative error ~5e-8)
       // and two Newton steps (y *= 1.5 - 0.5 a y^2 each) bring it within
       // 2.4e-16 (measured over 2^20 values spanning 2^+-100), against 1.7e-16
-      // for a rounded square root and division, at a third of the instructions
+      // for a rounded square root and division, with fewer instructions
       const double a = ss / (double)D + (double)p.eps;
       double inv = __builtin_amdgcn_rsq(a);
       inv = inv * fma(-0.5 * a * inv, inv, 1.5);
