@@ -272,13 +272,18 @@ def measure_norms(cfg: W.Config, torch, sdit, steps: int, warmup: int):
     return res
 
 
-def _time_rotating(torch, fn, n_sets: int, steps: int, warmup: int):
+def _time_rotating(torch, fn, n_sets: int, steps: int, warmup: int, settle_s: float = 0.2):
     """Median, p10 and p90 (us) of single launches fn(i), timed with HIP
-    events on the current stream, cycling through n_sets buffer sets."""
+    events on the current stream, cycling through n_sets buffer sets (after
+    about settle_s seconds of untimed launches and the warmup ones)."""
     stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < settle_s:
+        fn(i % n_sets)
+        i += 1
     for i in range(warmup):
         fn(i % n_sets)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i, (a, b) in enumerate(evs):
         a.record(stream)
         fn(i % n_sets)
@@ -440,15 +445,45 @@ def cpu_baseline(cfg: W.Config, budget_s: float = 10.0):
                 + [f"attention for {heads} of {cfg.n_heads} heads"]) + f", fp64 numpy, {el:.1f} s"}
 
 
-def time_step(step: "Step", torch, steps: int, warmup: int, with_merge: bool = False):
-    """W untimed steps, then K steps bracketed by events; per-step attention
-    events on the launch stream. Returns (ms per step, attention ms per call
-    list, events, wall seconds)."""
-    for _ in range(warmup):
+# Untimed steps run back to back before the warmup steps, for at least this
+# long: from idle the engine clock needs a few hundred milliseconds of
+# continuous load to reach its sustained level (measured on MI355X: ~1.1 GHz
+# at the start of a Wan-chunk run, ~2.2 GHz after 0.3-0.5 s, the attention
+# call 0.69 ms over the first 20 steps and 0.60 ms from step ~50 on).
+SETTLE_S = 0.5
+
+
+def settle_clock(step: "Step", torch, seconds: float):
+    """Run untimed steps back to back for about ``seconds`` (step count from a
+    short timed probe), so that the timed steps run at the sustained clock.
+    Returns (steps run, wall seconds)."""
+    if seconds <= 0:
+        return 0, 0.0
+    t0 = time.perf_counter()
+    for _ in range(3):
         step.run()
     torch.cuda.synchronize()
+    per = max((time.perf_counter() - t0) / 3, 1e-5)
+    n = int(min(20000, max(1, seconds / per)))
+    for _ in range(n):
+        step.run()
+    torch.cuda.synchronize()
+    return n + 3, time.perf_counter() - t0
+
+
+def time_step(step: "Step", torch, steps: int, warmup: int, with_merge: bool = False,
+              settle_s: float = SETTLE_S):
+    """Clock settling (untimed steps for settle_s seconds), W untimed steps,
+    then K steps bracketed by events; per-step attention events on the launch
+    stream. The events exist before the untimed steps start, so nothing but a
+    synchronisation separates the last untimed step from the first timed one.
+    Returns (ms per step, attention ms per call list, events, wall seconds,
+    (settle steps, settle seconds))."""
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3 if with_merge else 2)) for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    settle = settle_clock(step, torch, settle_s)
+    for _ in range(warmup):
+        step.run()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
@@ -457,17 +492,18 @@ def time_step(step: "Step", torch, steps: int, warmup: int, with_merge: bool = F
     end.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    return start.elapsed_time(end) / steps, [e[0].elapsed_time(e[1]) for e in evs], evs, t_wall
+    return start.elapsed_time(end) / steps, [e[0].elapsed_time(e[1]) for e in evs], evs, t_wall, settle
 
 
 def config_record(cfg: W.Config, torch, sdit, steps: int, warmup: int, cpu_budget: float, step=None, timing=None,
-                  cpu=None):
+                  cpu=None, settle_s: float = SETTLE_S):
     """One workload's record for the ``configs`` object: the balanced
     attention call of the library's plan inside the full step (``step`` and
     ``timing`` reuse the headline measurement, ``cpu`` its oracle timing)."""
     if step is None:
         step = Step(cfg, torch, sdit)
-    ms_step, attn_ms, _, _ = timing if timing is not None else time_step(step, torch, steps, warmup)
+    ms_step, attn_ms, _, _, _ = (timing if timing is not None
+                                 else time_step(step, torch, steps, warmup, settle_s=settle_s))
     a = np.asarray(attn_ms)
     med = float(np.median(a))
     rec = {"description": cfg.description, "n_heads": cfg.n_heads, "head_dim": cfg.head_dim, "n_q": cfg.n_q,
@@ -503,6 +539,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="seconds of untimed steps before the warmup steps (engine clock ramp; 0: none)")
     ap.add_argument("--workload", default="wan13b", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -553,18 +591,18 @@ def main():
     clocks = {"before": read_clocks()}
     step = Step(cfg, torch, sdit, args.kv_parts, args.launch, args.split_tile,
                 fused_cache_write=not args.unfused_cache_write)
-    for _ in range(args.warmup):
-        step.run()
-    torch.cuda.synchronize()
-
     # determinism: the output of two identical steps must be bit-identical
+    # (checked first: the host-side hashing leaves the GPU idle)
+    step.run()
+    torch.cuda.synchronize()
     h1 = hashlib.md5(step.out.cpu().numpy().tobytes()).hexdigest()
     step.run()
     torch.cuda.synchronize()
     h2 = hashlib.md5(step.out.cpu().numpy().tobytes()).hexdigest()
 
-    timing = time_step(step, torch, args.steps, 0, with_merge=args.kv_parts > 1)
-    ms_step, attn_ms, evs, t_wall = timing
+    timing = time_step(step, torch, args.steps, args.warmup, with_merge=args.kv_parts > 1,
+                       settle_s=args.settle_s)
+    ms_step, attn_ms, evs, t_wall, settle = timing
     clocks["after"] = read_clocks()
     attn_avg = float(np.mean(attn_ms))
     value = step.flops / (ms_step * 1e-3) / 1e12
@@ -600,6 +638,9 @@ def main():
         "device": device_info(torch),
         "clocks": clocks,
         "wall_s_timed": round(t_wall, 3),
+        "clock_settle": {"untimed_steps": settle[0], "seconds": round(settle[1], 3),
+                         "note": "untimed steps run back to back before the warmup steps, so that the "
+                                 "timed steps see the sustained engine clock"},
         "roofline": {"kernel": (f"attn_fwd_kernel<{cfg.head_dim}>"
                                + (f" + attn_split_merge_kernel<{cfg.head_dim}>" if step.plan[0] > 0 else "")),
                      "bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS,
@@ -631,7 +672,8 @@ def main():
                                               timing=timing, cpu=rec.get("cpu_baseline"))
             else:
                 c = W.WORKLOADS[name]
-                configs[name] = config_record(c, torch, sdit, args.steps, args.warmup, cpu_budget)
+                configs[name] = config_record(c, torch, sdit, args.steps, args.warmup, cpu_budget,
+                                              settle_s=args.settle_s)
                 torch.cuda.empty_cache()
         rec["configs"] = configs
         rec["clocks"]["after_configs"] = read_clocks()

@@ -56,6 +56,8 @@ def test_bench_prints_one_contract_line():
     assert r["n_gpus"] == 1 and r["steps"] == 3 and r["warmup"] == 1
     assert r["higher_is_better"] is True and r["data"] == "synthetic" and r["dtype"].startswith("bf16")
     assert r["config"]["workload"] == "wan13b" and r["value"] > 0 and r["ms_per_step"] > 0
+    # untimed clock-settling steps ran before the warmup steps, and say so
+    assert r["clock_settle"]["untimed_steps"] >= 1 and r["clock_settle"]["seconds"] > 0
     rf = r["roofline"]
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 2500.0
     assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], abs=1e-4)
