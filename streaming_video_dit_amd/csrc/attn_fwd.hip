@@ -28,9 +28,11 @@
 //    register loads is issued between its score MFMAs rather than all at
 //    once (a burst from every wave queues in the CU's address unit and
 //    stalls the issuing waves).
-//  * Who moves the tiles differs by kernel. Without int8 segments the four
-//    leading waves load and stage every tile one step ahead (the lagging
-//    waves are the critical path there). With int8 segments all eight waves
+//  * Who moves the tiles differs by kernel. Without int8 segments every tile
+//    is loaded one step ahead: the four leading waves issue the direct K
+//    loads and all eight waves stage a share of V, each during its own score
+//    MFMAs (half the staging registers per thread of four staging waves,
+//    measured 0.6-1% faster). With int8 segments all eight waves
 //    stage (the int8 tiles need the registers), two steps ahead: each wave
 //    commits its share of tile i+1 in step i, the leading waves first (then
 //    scores, softmax, P.V: vector, matrix, vector, matrix), the lagging ones
@@ -147,9 +149,7 @@ struct Layout {
 // Who moves a tile. bf16 K goes from global memory straight into LDS,
 // issued by the first KW waves (the ones that run ahead). V (bf16 -> fp16)
 // and int8 K/V codes are staged through the registers of the first ST
-// threads: the four leading waves in unscaled kernels (there the lagging
-// waves are the critical path), all eight waves in scaled kernels (the
-// staged int8 tiles need the registers).
+// threads: all eight waves in every kernel (ST = NT).
 template <int D, int ST>
 struct Loader {
   static constexpr int KW = NW / 2;
@@ -890,7 +890,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   // 16*(g16&1) + 4*(s16&3) inside each 32-column tile
   const int v_lane = (4 * hh + (s16 >> 2)) * L::VS + 16 * (g16 & 1) + 4 * (s16 & 3);
 
-  constexpr int ST = SCALED ? NT : NT / 2;   // staging threads (see Loader)
+  constexpr int ST = NT;   // staging threads (see Loader)
   using LD = Loader<D, ST>;
   Stage<D, ST, SCALED> st;
   LoadPlan<D, ST> plan;
@@ -988,7 +988,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll 1
       for (int it = 0; it < total; ++it) {
         const TileRef t = tile_at<D, GENERAL>(p, sm, it);
-        const bool direct_k = SCALED ? (k_wave && !t.is_int8) : stager;
+        const bool direct_k = k_wave && !(SCALED && t.is_int8);
         if (direct_k) issue_kdma<D, ST>(p, t, head, sm, it & 1, plan);
         if (stager) issue_stage<D, ST, SCALED>(p, t, head, st, plan);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1005,18 +1005,18 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         __syncthreads();
       }
     } else if constexpr (!SCALED) {
-      // ---- unscaled kernels: the four leading waves move every tile one
-      // step ahead. Tile i lives in K buffer i%2 and V buffer i%3. During
-      // step i the leading waves' V loads of tile i+1 ride on their score
-      // MFMAs and its direct K loads follow the last score MFMA (the compiler
-      // waits for every LDS read in flight after one of those, which inside
-      // the MFMA sequence drained the operand prefetch); its V is converted
-      // and stored at the end of the step. Waves 4..7 run half a tile behind:
+      // ---- unscaled kernels: every tile moves one step ahead. Tile i lives
+      // in K buffer i%2 and V buffer i%3. During step i every wave's V loads
+      // of tile i+1 ride on its score MFMAs, and the leading waves' direct K
+      // loads follow their last score MFMA (the compiler waits for every LDS
+      // read in flight after one of those, which inside the MFMA sequence
+      // drained the operand prefetch); V is converted and stored at the end
+      // of the step. Waves 4..7 run half a tile behind:
       // they multiply the previous tile's P with V first, then compute the
       // current tile's scores and softmax.
       TileRef tn = tile_at<D, GENERAL>(p, sm, 0);
       if (stager) {
-        issue_kdma<D, ST>(p, tn, head, sm, 0, plan);
+        if (k_wave) issue_kdma<D, ST>(p, tn, head, sm, 0, plan);
         issue_stage<D, ST, SCALED>(p, tn, head, st, plan);
         commit_tile<D, ST, SCALED>(p, tn, st, sm, 0, 0, 0, i8_min_scale);
       }
@@ -1053,14 +1053,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
                   issue_stage_part<D, ST, SCALED>(p, tn, head, st, plan, i / STRIDE);
               },
               [&]() {
-                if (stager && has_next) issue_kdma<D, ST>(p, tn, head, sm, knext, plan);
+                if (k_wave && has_next) issue_kdma<D, ST>(p, tn, head, sm, knext, plan);
               });
           if (lagging)
             pending = true;
           else
             pv_tile<D, PF_PV>(ws, sm.v[vbuf], v_lane, pb);
         } else if (has_next && stager) {
-          issue_kdma<D, ST>(p, tn, head, sm, knext, plan);
+          if (k_wave) issue_kdma<D, ST>(p, tn, head, sm, knext, plan);
           issue_stage<D, ST, SCALED>(p, tn, head, st, plan);
         }
         if (has_next && stager) commit_tile<D, ST, SCALED>(p, tn, st, sm, knext, vnext, 0, i8_min_scale);
