@@ -646,6 +646,10 @@ __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t
 #pragma unroll
     for (int i = 0; i < PF; ++i)
       ka[i] = *reinterpret_cast<const bf16x8*>(kl + k_lane + (i / NKS) * 32 * L::KS + (i % NKS) * 16);
+    // the score and P.V MFMA sequences run at raised wave priority (the
+    // SIMD's arbiter then favours the wave issuing matrix work; measured with
+    // a settled clock: 0.3-0.7% faster on every workload)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const bf16x8 a = ka[i % PF];
@@ -657,6 +661,7 @@ __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   after_scores();
 
   // ---- masking bias: one extra k-step. Lane (key, hh) supplies A[key][slot]
@@ -759,6 +764,7 @@ __device__ __forceinline__ void pv_tile(WaveState<D>& ws, const uint16_t* vl, in
   f16x8 va[PF];
 #pragma unroll
   for (int i = 0; i < PF; ++i) va[i] = read_vt<D>(vl, v_lane, i / 4, i % 4);
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int i = 0; i < NPV; ++i) {
     const f16x8 a = va[i % PF];
@@ -766,6 +772,7 @@ __device__ __forceinline__ void pv_tile(WaveState<D>& ws, const uint16_t* vl, in
     ws.o[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[i % 4], ws.o[i / 4], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Scaled kernels, leading waves: the next tile's direct K loads, then scores,
