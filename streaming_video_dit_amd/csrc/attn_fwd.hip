@@ -111,6 +111,25 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Buffer resource over the bytes [base, base + n_bytes): raw (stride 0),
+// word 3 = the gfx9 32-bit data format. A tile's loads address it with one
+// 32-bit per-lane offset (no 64-bit address arithmetic in the loop), and a
+// load at or past n_bytes reads zeros without touching memory: that is how
+// the rows past a segment end are read.
+// Both arguments are wave-uniform; readfirstlane states it, so the compiler
+// never wraps a load in a loop over distinct resources.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t n_bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
+                     ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)u, (short)0, __builtin_amdgcn_readfirstlane((int)n_bytes), 0x00020000);
+}
+// 16 bytes per lane from the resource at byte offset off straight into LDS:
+// lane t lands at lds_dst + 16 t
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rs, void* lds_dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_dst, 16, off, 0, 0, 0);
+}
+
 constexpr int BQ = kAttnBQ;
 constexpr int BK = kAttnBK;
 constexpr int NW = 8;                 // waves per workgroup, 32 query rows each
@@ -374,18 +393,19 @@ struct Stage {
   float ks, vs;
 };
 
-// Per-thread load geometry, fixed for the whole kernel: element offsets (from
-// a tile's first row, head included) of every chunk this thread moves.
+// Per-thread load geometry, fixed for the whole kernel: byte offsets, from a
+// tile's first row (head included), of every chunk this thread moves.
 template <int D, int ST>
 struct LoadPlan {
   static constexpr int KMAX = Loader<D, ST>::KMAX;
-  int k_off[KMAX];   // bf16 K (K waves), padded-tile block wave + KW*i (padding chunks reload chunk 0)
-  int v_off;         // bf16 V chunk j adds j * (ST / CPR) rows
-  int i8_off;        // int8 K/V chunk j adds j * (ST / (D/16)) rows
+  static constexpr int VCH = Loader<D, ST>::VCH;
+  uint32_t k_off[KMAX];   // bf16 K (K waves), padded-tile block wave + KW*i (padding chunks reload chunk 0)
+  uint32_t v_off[VCH];    // bf16 V chunk j: rows j * (ST / CPR) further down
+  uint32_t i8_off;        // int8 K/V codes (one chunk)
 };
 
 template <int D, int ST>
-__device__ __forceinline__ void make_plan(LoadPlan<D, ST>& pl, int row_stride) {
+__device__ __forceinline__ void make_plan(LoadPlan<D, ST>& pl, uint32_t row_bytes) {
   using L = Layout<D>;
   constexpr int KW = Loader<D, ST>::KW;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -393,37 +413,36 @@ __device__ __forceinline__ void make_plan(LoadPlan<D, ST>& pl, int row_stride) {
   for (int i = 0; i < LoadPlan<D, ST>::KMAX; ++i) {
     const int lin = (wave + KW * i) * 64 + lane;
     const int row = lin / L::K_CH, pc = lin % L::K_CH;
-    pl.k_off[i] = row * row_stride + (pc < L::CPR ? pc : 0) * 8;
+    pl.k_off[i] = row * row_bytes + (pc < L::CPR ? pc : 0) * 16;
   }
-  pl.v_off = (tid / L::CPR) * row_stride + (tid % L::CPR) * 8;
-  pl.i8_off = (tid / (D / 16)) * row_stride + (tid % (D / 16)) * 16;
+#pragma unroll
+  for (int j = 0; j < LoadPlan<D, ST>::VCH; ++j)
+    pl.v_off[j] = (tid / L::CPR + j * (ST / L::CPR)) * row_bytes + (tid % L::CPR) * 16;
+  // int8 rows are half as long as bf16 rows
+  pl.i8_off = (tid / (D / 16)) * (row_bytes / 2) + (tid % (D / 16)) * 16;
 }
 
 // bf16 K of tile t straight into LDS buffer kbuf (K waves only). Rows past
-// the segment end are loaded from its last row: their scores get the -1e30
-// bias, so their probabilities are exactly 0 and any finite data there is
-// harmless.
+// the segment end read as zeros (the tile's buffer resource ends with the
+// segment): their scores get the -1e30 bias, so their probabilities are
+// exactly 0.
 template <int D, int ST>
 __device__ __forceinline__ void issue_kdma_to(const AttnParams& p, const TileRef& t, int head, uint16_t* kdst,
                                               const LoadPlan<D, ST>& pl) {
   using L = Layout<D>;
   constexpr int KW = Loader<D, ST>::KW;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row_stride = p.n_heads * D;
-  const uint16_t* kb = (const uint16_t*)t.k + ((int64_t)t.key0 * p.n_heads + head) * D;
-  const bool ragged = t.n_valid < BK;
+  // only the K waves (0..KW-1) get here; the mask tells the compiler so, and
+  // readfirstlane keeps the LDS destinations in scalar registers
+  static_assert((KW & (KW - 1)) == 0, "KW is a power of two");
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (KW - 1);
+  const uint32_t row_bytes = (uint32_t)p.n_heads * D * 2;
+  const auto rs = tile_rsrc((const uint16_t*)t.k + ((int64_t)t.key0 * p.n_heads + head) * D,
+                            (uint32_t)t.n_valid * row_bytes);
 #pragma unroll
   for (int j = 0; j < Loader<D, ST>::KMAX; ++j) {
     const int blk = wave + KW * j;
-    if (blk < L::K_BLKS) {
-      int off = pl.k_off[j];
-      if (ragged) {
-        const int lin = blk * 64 + lane;
-        const int row = lin / L::K_CH, pc = lin % L::K_CH;
-        off = min(row, t.n_valid - 1) * row_stride + (pc < L::CPR ? pc : 0) * 8;
-      }
-      __builtin_amdgcn_global_load_lds((const void*)(kb + off), (lds_void*)(kdst + blk * 64 * 8), 16, 0, 0);
-    }
+    if (blk < L::K_BLKS)
+      buffer_to_lds16(rs, kdst + blk * 64 * 8, pl.k_off[j]);
   }
 }
 
@@ -444,29 +463,20 @@ __device__ __forceinline__ void issue_stage_part(const AttnParams& p, const Tile
   using L = Layout<D>;
   using LD = Loader<D, ST>;
   const int tid = threadIdx.x;
-  const int row_stride = p.n_heads * D;
   const int64_t base = ((int64_t)t.key0 * p.n_heads + head) * D;
-  const bool ragged = t.n_valid < BK;
   static_assert(!SCALED || LD::I8CH == 1, "a staging thread moves one row's 16 K and 16 V codes");
   if (!SCALED || !t.is_int8) {
     if (j < LD::VCH) {
-      const uint16_t* vb = (const uint16_t*)t.v + base;
-      constexpr int RSTEP = ST / L::CPR;
-      int off = pl.v_off + j * RSTEP * row_stride;
-      if (ragged) off = min(tid / L::CPR + j * RSTEP, t.n_valid - 1) * row_stride + (tid % L::CPR) * 8;
-      st.r[j] = *reinterpret_cast<const uint4*>(vb + off);
+      // rows past the segment end read as zeros (their probabilities are 0)
+      const auto rs = tile_rsrc((const uint16_t*)t.v + base, (uint32_t)t.n_valid * p.n_heads * D * 2);
+      st.r[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, pl.v_off[j], 0, 0));
     }
   } else {
     if (j < 2 * LD::I8CH) {
       if (LD::I8_THREADS >= ST || tid < LD::I8_THREADS) {
-        const int ji = j % LD::I8CH;
-        constexpr int RSTEP = ST / (D / 16);
-        int off = pl.i8_off + ji * RSTEP * row_stride;
-        if (ragged) off = min(tid / (D / 16) + ji * RSTEP, t.n_valid - 1) * row_stride + (tid % (D / 16)) * 16;
-        if (j < LD::I8CH)
-          st.r[ji] = *reinterpret_cast<const uint4*>((const int8_t*)t.k + base + off);
-        else
-          st.r[LD::I8CH + ji] = *reinterpret_cast<const uint4*>((const int8_t*)t.v + base + off);
+        // zero codes past the segment end (their keys are masked, their P is 0)
+        const auto rs = tile_rsrc((const int8_t*)(j < LD::I8CH ? t.k : t.v) + base, (uint32_t)t.n_valid * p.n_heads * D);
+        st.r[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, pl.i8_off, 0, 0));
       }
     } else if (j == 2 * LD::I8CH) {
       if (tid < BK) st.ks = t.k_scale[(int64_t)(t.key0 + min(tid, t.n_valid - 1)) * p.n_heads + head];
@@ -901,7 +911,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   using LD = Loader<D, ST>;
   Stage<D, ST, SCALED> st;
   LoadPlan<D, ST> plan;
-  make_plan<D, ST>(plan, p.n_heads * D);
+  make_plan<D, ST>(plan, (uint32_t)p.n_heads * D * 2);
   constexpr int NPART = LD::template npart<SCALED>();
   constexpr int STRIDE = (2 * NKS) / NPART;
   const bool k_wave = wave < LD::KW;
