@@ -612,19 +612,18 @@ struct WaveState {
   int e_o;             // o holds O * 2^e_o (the V exponent of the tiles last multiplied)
 };
 
-// First half of a 64-key tile for one wave: S^T = K Q^T, masking bias,
-// online softmax; leaves P^T (fp16, B-operand layout) in pb. after_mfma(i)
-// runs after the i-th of the 2*D/16 score MFMAs, after_scores() after the
-// last one. Element e2 of
-// score subtile kt is key kt*32 + 8*(e2/4) + 4*hh + e2%4 of the tile.
-template <int D, bool SCALED, bool GENERAL, bool EXACT, typename Hook, typename Tail>
-__device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t, WaveState<D>& ws,
+// S^T = K Q^T for the two 32-key subtiles of a 64-key tile, plus the masking
+// bias, for one wave; int8 tiles of the scaled kernels multiplied per key.
+// Returns the factor that brings s to log2 units. after_mfma(i) runs after
+// the i-th of the 2*D/16 score MFMAs, after_scores() after the last one.
+// Element e2 of subtile kt is key kt*32 + 8*(e2/4) + 4*hh + e2%4 of the tile.
+template <int D, bool SCALED, bool GENERAL, typename Hook, typename Tail>
+__device__ __forceinline__ float qk_scores(const AttnParams& p, const TileRef& t, WaveState<D>& ws,
                                            const uint16_t* kl, const float* ksc, int k_lane,
-                                           int r, int hh, int my_qb, int qb_lo, int n_qbt, f16x8 (&pb)[4],
-                                           int e, Hook&& after_mfma, Tail&& after_scores) {
+                                           int r, int hh, int my_qb, int qb_lo, f32x16 (&s)[2],
+                                           Hook&& after_mfma, Tail&& after_scores) {
   using L = Layout<D>;
   constexpr int NKS = D / 16;
-  constexpr int NDT = D / 32;
   // LDS operand reads in flight ahead of their MFMA (the scaled path needs the registers)
   constexpr int PF = SCALED ? 2 : 4;
 
@@ -646,7 +645,6 @@ __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t
   // ---- S^T = K Q^T for two 32-key subtiles; operand reads PF steps ahead,
   // scheduling fences keep the compiler from hoisting all of them
   constexpr int NQK = 2 * NKS;
-  f32x16 s[2];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -701,85 +699,121 @@ __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t
     }
   }
 
-  // ---- scores in log2 units and the tile's row max
-  float mt = -INFINITY;
   if (per_key) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) scale_by_row_lanes<0>(s[kt], kmul[kt]);
   }
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int e2 = 0; e2 < 16; e2 += 2) mt = max3(mt, s[kt][e2], s[kt][e2 + 1]);
-  const float cs = per_key ? 1.0f : p.scale_log2;
-  mt = swap_halves_max(mt) * cs;
-  if (mt < MASKED_MAX) mt = -INFINITY;   // nothing visible for this row in the tile
+  return per_key ? 1.0f : p.scale_log2;
+}
 
-  // ---- online softmax (lazy running max). The same rare branch brings o to
-  // the tile's V exponent e (exact power-of-two rescale), before the P.V of
-  // this tile adds to it.
-  const bool need = mt > ws.m_run + TAU;
-  if (__ballot(need) || (EXACT && e != ws.e_o)) {
-    const float m_new = need ? mt : ws.m_run;
-    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(ws.m_run - m_new);
-    ws.m_run = m_new;
-    ws.l_run *= alpha;
-    const int sh = EXACT ? e - ws.e_o : 0;
-    ws.e_o = EXACT ? e : ws.e_o;
-    if (sh == 0) {
-#pragma unroll
-      for (int i = 0; i < NDT; ++i)
-#pragma unroll
-        for (int e2 = 0; e2 < 16; ++e2) ws.o[i][e2] *= alpha;
-    } else {
-#pragma unroll
-      for (int i = 0; i < NDT; ++i)
-#pragma unroll
-        for (int e2 = 0; e2 < 16; ++e2) ws.o[i][e2] = ldexpf(ws.o[i][e2] * alpha, sh);
-    }
-  }
-  const float m_use = (ws.m_run == -INFINITY) ? 0.f : ws.m_run;
+// Group kk (0..3) of a tile's scores: subtile kk/2, elements 8(kk%2)..+7,
+// which are P^T B-operand kk of the P.V MFMAs.
+__device__ __forceinline__ float score_of(const f32x16 (&s)[2], int kk, int j) { return s[kk >> 1][8 * (kk & 1) + j]; }
 
-  f16x2 ones;
-  ones[0] = (_Float16)1.0f;
-  ones[1] = (_Float16)1.0f;
+// P of group kk in fp16 and the sum of those fp16 values into lt (pairs in
+// order, fp32 accumulation)
+__device__ __forceinline__ f16x8 pack_group(const float (&f)[8], float& lt) {
+  f16x8 v;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    float pv[16];
+  for (int j = 0; j < 8; ++j) v[j] = (_Float16)f[j];
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int e2 = 0; e2 < 16; ++e2) pv[e2] = __builtin_amdgcn_exp2f(fmaf(s[kt][e2], cs, -m_use));
+  for (int j = 0; j < 8; j += 2) lt = __builtin_amdgcn_fdot2(f16x2{v[j], v[j + 1]}, ones, lt, false);
+  return v;
+}
+
+// P = 2^(s cs - m) for a whole tile into pb; lt = sum of this lane's P
+__device__ __forceinline__ void exp_tile(const f32x16 (&s)[2], float cs, float m, f16x8 (&pb)[4], float& lt) {
+  lt = 0.f;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      f16x8 v;
+  for (int kk = 0; kk < 4; ++kk) {
+    float f[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = (_Float16)pv[8 * half + j];
-      pb[2 * kt + half] = v;
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        f16x2 pr;
-        pr[0] = v[j];
-        pr[1] = v[j + 1];
-        ws.l_run = __builtin_amdgcn_fdot2(pr, ones, ws.l_run, false);
-      }
-    }
+    for (int j = 0; j < 8; ++j) f[j] = __builtin_amdgcn_exp2f(fmaf(score_of(s, kk, j), cs, -m));
+    pb[kk] = pack_group(f, lt);
   }
 }
 
+// Online softmax with a lazy running max: O and l are only rescaled when a
+// row's max grows by more than 2^TAU, so P stays <= 2^TAU. The exponentials
+// are taken first with the running max as it stands; a lane whose P sum
+// stays below 2^TAU has every P below it, so no row max is needed then. Only
+// when some lane reaches it (or a row has seen nothing yet) does the wave
+// take the tile's row max; if a row max has grown past the threshold, O and
+// l are rescaled and the exponentials taken again. The same rare branch
+// brings o to the tile's V exponent e (exact power-of-two rescale). Runs
+// after every earlier tile's P.V has reached o.
+template <int D, bool EXACT>
+__device__ __forceinline__ void settle_tile(WaveState<D>& ws, const f32x16 (&s)[2], float cs, f16x8 (&pb)[4],
+                                            float lt, int e) {
+  constexpr int NDT = D / 32;
+  static_assert(TAU == 8.0f, "threshold below is 2^TAU");
+  const bool suspect = ws.m_run == -INFINITY || !(lt < 0x1p8f);
+  if (__ballot(suspect) || (EXACT && e != ws.e_o)) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e2 = 0; e2 < 16; e2 += 2) mt = max3(mt, s[kt][e2], s[kt][e2 + 1]);
+    mt = swap_halves_max(mt) * cs;
+    if (mt < MASKED_MAX) mt = -INFINITY;   // nothing visible for this row in the tile
+    const bool need = mt > ws.m_run + TAU;
+    const bool grow = __ballot(need) != 0;
+    if (grow || (EXACT && e != ws.e_o)) {
+      const float m_new = need ? mt : ws.m_run;
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(ws.m_run - m_new);
+      ws.m_run = m_new;
+      ws.l_run *= alpha;
+      const int sh = EXACT ? e - ws.e_o : 0;
+      ws.e_o = EXACT ? e : ws.e_o;
+      if (sh == 0) {
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+          for (int e2 = 0; e2 < 16; ++e2) ws.o[i][e2] *= alpha;
+      } else {
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+          for (int e2 = 0; e2 < 16; ++e2) ws.o[i][e2] = ldexpf(ws.o[i][e2] * alpha, sh);
+      }
+    }
+    if (grow) exp_tile(s, cs, (ws.m_run == -INFINITY) ? 0.f : ws.m_run, pb, lt);
+  }
+  ws.l_run += lt;
+}
+
+// A whole tile for one wave: scores, then the softmax (P^T left in pb).
+template <int D, bool SCALED, bool GENERAL, bool EXACT, typename Hook, typename Tail>
+__device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t, WaveState<D>& ws,
+                                           const uint16_t* kl, const float* ksc, int k_lane,
+                                           int r, int hh, int my_qb, int qb_lo, f16x8 (&pb)[4],
+                                           int e, Hook&& after_mfma, Tail&& after_scores) {
+  f32x16 s[2];
+  const float cs = qk_scores<D, SCALED, GENERAL>(p, t, ws, kl, ksc, k_lane, r, hh, my_qb, qb_lo, s, after_mfma,
+                                                 after_scores);
+  float lt;
+  exp_tile(s, cs, (ws.m_run == -INFINITY) ? 0.f : ws.m_run, pb, lt);
+  settle_tile<D, EXACT>(ws, s, cs, pb, lt, e);
+}
+
 // Second half of a tile: O^T += V^T P^T (transposed reads of the row-major
-// fp16 V tile, which holds V * 2^e; qk_softmax of the tile has brought o to
-// the same exponent).
+// fp16 V tile, which holds V * 2^e; the tile's settle_tile has brought o to
+// the same exponent). MFMA i multiplies key group kk = i / NDT into column
+// tile dt = i % NDT.
 template <int D, int PF>
 __device__ __forceinline__ void pv_tile(WaveState<D>& ws, const uint16_t* vl, int v_lane, const f16x8 (&pb)[4]) {
-  constexpr int NPV = 4 * (D / 32);
+  constexpr int NDT = D / 32;
+  constexpr int NPV = 4 * NDT;
   f16x8 va[PF];
 #pragma unroll
-  for (int i = 0; i < PF; ++i) va[i] = read_vt<D>(vl, v_lane, i / 4, i % 4);
+  for (int i = 0; i < PF; ++i) va[i] = read_vt<D>(vl, v_lane, i % NDT, i / NDT);
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int i = 0; i < NPV; ++i) {
     const f16x8 a = va[i % PF];
-    if (i + PF < NPV) va[i % PF] = read_vt<D>(vl, v_lane, (i + PF) / 4, (i + PF) % 4);
-    ws.o[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[i % 4], ws.o[i / 4], 0, 0, 0);
+    if (i + PF < NPV) va[i % PF] = read_vt<D>(vl, v_lane, (i + PF) % NDT, (i + PF) / NDT);
+    ws.o[i % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[i / NDT], ws.o[i % NDT], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_setprio(0);
@@ -797,10 +831,10 @@ __device__ __forceinline__ void lead_tile_scaled(const AttnParams& p, const Tile
                                                  const float* __restrict__ ksc,
                                                  const uint16_t* __restrict__ vcur, uint16_t* __restrict__ knew,
                                                  bool dma, const LoadPlan<D, ST>& plan, int k_lane, int v_lane,
-                                                 int r, int hh, int my_qb, int qb_lo, int n_qbt, f16x8 (&pb)[4],
+                                                 int r, int hh, int my_qb, int qb_lo, f16x8 (&pb)[4],
                                                  Ride&& ride, int e) {
   if (dma) issue_kdma_to<D, ST>(p, tn, head, knew, plan);
-  qk_softmax<D, SCALED, GENERAL, EXACT>(p, t, ws, kcur, ksc, k_lane, r, hh, my_qb, qb_lo, n_qbt, pb, e, ride, [] {});
+  qk_softmax<D, SCALED, GENERAL, EXACT>(p, t, ws, kcur, ksc, k_lane, r, hh, my_qb, qb_lo, pb, e, ride, [] {});
   pv_tile<D, PF>(ws, vcur, v_lane, pb);
 }
 
@@ -875,7 +909,6 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   const int q_lo = qt * BQ;
   const int q_hi = min(p.n_q, q_lo + BQ) - 1;
   const int qb_lo = q_lo / p.block_q, qb_hi = q_hi / p.block_q;
-  const int n_qbt = qb_hi - qb_lo + 1;
   const int my_qb = min(q_row, p.n_q - 1) / p.block_q;
 
   WaveState<D> ws;
@@ -1016,7 +1049,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         if ((t.wmask >> wave) & 1) {
           f16x8 pb[4];
           qk_softmax<D, SCALED, GENERAL, EXACT>(p, t, ws, sm.k[it & 1], sm.ksc[it & 1], k_lane, r, hh, my_qb, qb_lo,
-                                                n_qbt, pb, e, [](int) {}, [] {});
+                                                pb, e, [](int) {}, [] {});
           pv_tile<D, PF_PV>(ws, sm.v[0], v_lane, pb);
         }
         __syncthreads();
@@ -1064,7 +1097,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         pending = false;
         if ((t.wmask >> wave) & 1) {
           qk_softmax<D, SCALED, GENERAL, EXACT>(
-              p, t, ws, sm.k[kbuf], sm.ksc[kbuf], k_lane, r, hh, my_qb, qb_lo, n_qbt, pb, e_it,
+              p, t, ws, sm.k[kbuf], sm.ksc[kbuf], k_lane, r, hh, my_qb, qb_lo, pb, e_it,
               [&](int i) {
                 if (stager && has_next && i % STRIDE == 0 && i / STRIDE < NPART)
                   issue_stage_part<D, ST, SCALED>(p, tn, head, st, plan, i / STRIDE);
@@ -1144,7 +1177,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
           if (compute) {
             lead_tile_scaled<D, SCALED, GENERAL, EXACT, ST, PF_PV>(p, t, tn1, head, ws, sm.k[kbuf], sm.ksc[kbuf],
                                                                    sm.v[vbuf], sm.k[knext], dma, plan,
-                                                                   k_lane, v_lane, r, hh, my_qb, qb_lo, n_qbt, pb,
+                                                                   k_lane, v_lane, r, hh, my_qb, qb_lo, pb,
                                                                    ride, e_cur);
           } else {
             if (dma) issue_kdma<D, ST>(p, tn1, head, sm, knext, plan);
@@ -1156,7 +1189,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
           if (has1) commit_tile<D, ST, SCALED>(p, tn1, st, sm, knext, vnext, e_next, i8_min_scale);
           if (compute) {
             qk_softmax<D, SCALED, GENERAL, EXACT>(p, t, ws, sm.k[kbuf], sm.ksc[kbuf], k_lane, r, hh, my_qb,
-                                                  qb_lo, n_qbt, pb, e_cur, ride, none);
+                                                  qb_lo, pb, e_cur, ride, none);
             pending = true;
           } else if (has2) {
             issue_stage<D, ST, SCALED>(p, tn2, head, st, plan);
