@@ -21,10 +21,12 @@
 //  * Keys stream through LDS in 64-key tiles, one barrier per tile. K is
 //    double buffered, V triple buffered (the lagging waves still read tile
 //    i-1 while tile i+1 is written). bf16 K goes straight from global memory
-//    into LDS (global_load_lds_dwordx4: lane t lands at base + 16 t, so each
-//    lane's source address is chosen to realise the padded layout below). V
-//    is staged through registers and converted to fp16; int8 K/V codes are
-//    widened exactly on the same path. Each wave's share of a tile's
+//    into LDS (buffer_load_dwordx4 ... lds: lane t lands at base + 16 t, so
+//    each lane's source offset is chosen to realise the padded layout below).
+//    V is staged through registers and converted to fp16; int8 K/V codes are
+//    widened exactly on the same path. Every tile load addresses a per-tile
+//    buffer resource with a fixed 32-bit per-lane offset (no address
+//    arithmetic in the loop); rows past a segment end read as zeros. Each wave's share of a tile's
 //    register loads is issued between its score MFMAs rather than all at
 //    once (a burst from every wave queues in the CU's address unit and
 //    stalls the issuing waves).
@@ -63,7 +65,9 @@
 //    bf16 V converts exactly for |v| < 65504; int8 codes always do.
 //  * Online softmax in base 2 (scale*log2(e) folded in), with a lazy running
 //    max: O and l are only rescaled when a row max grows by more than 2^8, so
-//    P stays <= 256 and the rescale is skipped for almost every tile.
+//    P stays <= 256 and the rescale is skipped for almost every tile. The
+//    exponentials are taken with the running max first; the tile's row max is
+//    only computed when some lane's P sum reaches 2^8.
 //  * Mask: each workgroup compacts the kept 64-key tiles of its 256 rows into
 //    an LDS list of packed descriptors (key offset, segment, valid keys, and
 //    which waves have a kept (q-block, k-block) pair in the tile), passes of
