@@ -398,7 +398,9 @@ struct Stage {
 };
 
 // Per-thread load geometry, fixed for the whole kernel: byte offsets, from a
-// tile's first row (head included), of every chunk this thread moves.
+// tile's first row (head included), of every chunk this thread moves. The
+// host allows at most 65536 heads, so a row is at most 2^24 bytes and every
+// offset and resource size within a 64-key tile stays below 2^30.
 template <int D, int ST>
 struct LoadPlan {
   static constexpr int KMAX = Loader<D, ST>::KMAX;
