@@ -32,9 +32,10 @@
 //    stalls the issuing waves).
 //  * Who moves the tiles differs by kernel. Without int8 segments every tile
 //    is loaded one step ahead: the four leading waves issue the direct K
-//    loads and all eight waves stage a share of V, each during its own score
-//    MFMAs (half the staging registers per thread of four staging waves,
-//    measured 0.6-1% faster). With int8 segments all eight waves
+//    loads and stage V, during their score MFMAs (they wait at the barrier
+//    for the lagging waves, which then carry none of the loading; measured
+//    1.5% faster than spreading V over all eight waves on the dense chunks,
+//    within noise on the block-sparse one). With int8 segments all eight waves
 //    stage (the int8 tiles need the registers), two steps ahead: each wave
 //    commits its share of tile i+1 in step i, the leading waves first (then
 //    scores, softmax, P.V: vector, matrix, vector, matrix), the lagging ones
@@ -172,7 +173,8 @@ struct Layout {
 // Who moves a tile. bf16 K goes from global memory straight into LDS,
 // issued by the first KW waves (the ones that run ahead). V (bf16 -> fp16)
 // and int8 K/V codes are staged through the registers of the first ST
-// threads: all eight waves in every kernel (ST = NT).
+// threads: the four leading waves in the unscaled kernels, all eight in
+// the scaled ones (the int8 tiles need the registers).
 template <int D, int ST>
 struct Loader {
   static constexpr int KW = NW / 2;
@@ -946,7 +948,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   // 16*(g16&1) + 4*(s16&3) inside each 32-column tile
   const int v_lane = (4 * hh + (s16 >> 2)) * L::VS + 16 * (g16 & 1) + 4 * (s16 & 3);
 
-  constexpr int ST = NT;   // staging threads (see Loader)
+  constexpr int ST = SCALED ? NT : NT / 2;   // staging threads (see Loader)
   using LD = Loader<D, ST>;
   Stage<D, ST, SCALED> st;
   LoadPlan<D, ST> plan;
