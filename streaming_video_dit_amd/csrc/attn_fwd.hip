@@ -651,7 +651,10 @@ __device__ __forceinline__ float qk_scores(const AttnParams& p, const TileRef& t
   }
 
   // ---- S^T = K Q^T for two 32-key subtiles; operand reads PF steps ahead,
-  // scheduling fences keep the compiler from hoisting all of them
+  // scheduling fences keep the compiler from hoisting all of them. MFMA i
+  // takes k-slice i/2 of subtile i%2: consecutive MFMAs feed different
+  // accumulators (each subtile still sums its slices in order), which
+  // measured 2-3% faster than finishing one subtile before the other.
   constexpr int NQK = 2 * NKS;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
@@ -661,7 +664,7 @@ __device__ __forceinline__ float qk_scores(const AttnParams& p, const TileRef& t
     bf16x8 ka[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i)
-      ka[i] = *reinterpret_cast<const bf16x8*>(kl + k_lane + (i / NKS) * 32 * L::KS + (i % NKS) * 16);
+      ka[i] = *reinterpret_cast<const bf16x8*>(kl + k_lane + (i % 2) * 32 * L::KS + (i / 2) * 16);
     // the score and P.V MFMA sequences run at raised wave priority (the
     // SIMD's arbiter then favours the wave issuing matrix work; measured with
     // a settled clock: 0.3-0.7% faster on every workload)
@@ -670,9 +673,9 @@ __device__ __forceinline__ float qk_scores(const AttnParams& p, const TileRef& t
     for (int i = 0; i < NQK; ++i) {
       const bf16x8 a = ka[i % PF];
       if (i + PF < NQK)
-        ka[i % PF] = *reinterpret_cast<const bf16x8*>(kl + k_lane + ((i + PF) / NKS) * 32 * L::KS +
-                                                      ((i + PF) % NKS) * 16);
-      s[i / NKS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.qf[i % NKS], s[i / NKS], 0, 0, 0);
+        ka[i % PF] = *reinterpret_cast<const bf16x8*>(kl + k_lane + ((i + PF) % 2) * 32 * L::KS +
+                                                      ((i + PF) / 2) * 16);
+      s[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ws.qf[i / 2], s[i % 2], 0, 0, 0);
       after_mfma(i);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -730,17 +733,32 @@ __device__ __forceinline__ f16x8 pack_group(const float (&f)[8], float& lt) {
   return v;
 }
 
-// P = 2^(s cs - m) for a whole tile into pb; lt = sum of this lane's P
+// P = 2^(s cs - m) for a whole tile into pb; lt = sum of this lane's P,
+// accumulated in NACC independent partial sums (group kk into sum kk % NACC,
+// added pairwise at the end): one chain of 16 dependent dot products would
+// hold the softmax up on its latency.
+template <int NACC>
 __device__ __forceinline__ void exp_tile(const f32x16 (&s)[2], float cs, float m, f16x8 (&pb)[4], float& lt) {
-  lt = 0.f;
+  static_assert(NACC == 2 || NACC == 4, "two or four partial sums");
+  float part[NACC];
+#pragma unroll
+  for (int a = 0; a < NACC; ++a) part[a] = 0.f;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     float f[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) f[j] = __builtin_amdgcn_exp2f(fmaf(score_of(s, kk, j), cs, -m));
-    pb[kk] = pack_group(f, lt);
+    pb[kk] = pack_group(f, part[kk % NACC]);
   }
+  if constexpr (NACC == 4)
+    lt = (part[0] + part[1]) + (part[2] + part[3]);
+  else
+    lt = part[0] + part[1];
 }
+// Partial sums of a tile's P per kernel kind, the faster count of each as
+// measured: two in the kernels with int8 segments, four in the others.
+template <bool SCALED>
+constexpr int kSumParts = SCALED ? 2 : 4;
 
 // Online softmax with a lazy running max: O and l are only rescaled when a
 // row's max grows by more than 2^TAU, so P stays <= 2^TAU. The exponentials
@@ -751,7 +769,7 @@ __device__ __forceinline__ void exp_tile(const f32x16 (&s)[2], float cs, float m
 // l are rescaled and the exponentials taken again. The same rare branch
 // brings o to the tile's V exponent e (exact power-of-two rescale). Runs
 // after every earlier tile's P.V has reached o.
-template <int D, bool EXACT>
+template <int D, bool EXACT, int NACC>
 __device__ __forceinline__ void settle_tile(WaveState<D>& ws, const f32x16 (&s)[2], float cs, f16x8 (&pb)[4],
                                             float lt, int e) {
   constexpr int NDT = D / 32;
@@ -786,7 +804,7 @@ __device__ __forceinline__ void settle_tile(WaveState<D>& ws, const f32x16 (&s)[
           for (int e2 = 0; e2 < 16; ++e2) ws.o[i][e2] = ldexpf(ws.o[i][e2] * alpha, sh);
       }
     }
-    if (grow) exp_tile(s, cs, (ws.m_run == -INFINITY) ? 0.f : ws.m_run, pb, lt);
+    if (grow) exp_tile<NACC>(s, cs, (ws.m_run == -INFINITY) ? 0.f : ws.m_run, pb, lt);
   }
   ws.l_run += lt;
 }
@@ -801,8 +819,8 @@ __device__ __forceinline__ void qk_softmax(const AttnParams& p, const TileRef& t
   const float cs = qk_scores<D, SCALED, GENERAL>(p, t, ws, kl, ksc, k_lane, r, hh, my_qb, qb_lo, s, after_mfma,
                                                  after_scores);
   float lt;
-  exp_tile(s, cs, (ws.m_run == -INFINITY) ? 0.f : ws.m_run, pb, lt);
-  settle_tile<D, EXACT>(ws, s, cs, pb, lt, e);
+  exp_tile<kSumParts<SCALED>>(s, cs, (ws.m_run == -INFINITY) ? 0.f : ws.m_run, pb, lt);
+  settle_tile<D, EXACT, kSumParts<SCALED>>(ws, s, cs, pb, lt, e);
 }
 
 // Second half of a tile: O^T += V^T P^T (transposed reads of the row-major
